@@ -1,0 +1,228 @@
+"""Torch-facing wrappers of the C ABI, with the same names as the C entry points.
+
+These functions only marshal arguments: they take device pointers, shapes and
+strides from torch tensors, allocate outputs / workspace with torch when the
+caller does not pass them, pass the current torch stream, and raise
+``PagedAttnError`` on a non-zero status.  No step of the attention runs here.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import PA_BF16, PA_F32, PA_FP16, PA_FP8_E4M3, PaKvDesc, check, load
+
+_DT = {torch.bfloat16: PA_BF16, torch.float16: PA_FP16, torch.float32: PA_F32,
+       torch.uint8: PA_FP8_E4M3}
+if hasattr(torch, "float8_e4m3fn"):
+    _DT[torch.float8_e4m3fn] = PA_FP8_E4M3
+_TORCH = {PA_BF16: torch.bfloat16, PA_FP16: torch.float16, PA_F32: torch.float32}
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    try:
+        return _DT[dt]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {dt}") from None
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def kv_desc(k: torch.Tensor, v: torch.Tensor, *, k_scale: float = 1.0, v_scale: float = 1.0,
+            num_pages: Optional[int] = None) -> PaKvDesc:
+    """Descriptor of paged K/V views shaped [pages, Hkv, page_size, D] with any strides
+    (head_dim contiguous), e.g. the two halves of a [pages, Hkv, P, 2*D] cache."""
+    if k.shape != v.shape or k.dim() != 4:
+        raise ValueError("k and v must both be [pages, Hkv, page_size, D]")
+    if k.stride() != v.stride() or k.stride(-1) != 1:
+        raise ValueError("k and v need equal strides and a contiguous head_dim")
+    pages, hkv, P, _ = k.shape
+    return PaKvDesc(k.data_ptr(), v.data_ptr(), k.stride(0), k.stride(1), k.stride(2), P, hkv,
+                    int(num_pages if num_pages is not None else pages), dtype_code(k.dtype),
+                    float(k_scale), float(v_scale))
+
+
+def kv_halves(kv_cache: torch.Tensor, head_dim: int):
+    """K and V views of a [pages, Hkv, page_size, 2*head_dim] cache (no copy)."""
+    return kv_cache[..., :head_dim], kv_cache[..., head_dim:]
+
+
+def resolve_splits(B, query_len, Hq, Hkv, D, page_size, bt_width, window=0, num_splits=0) -> int:
+    return int(load().paged_attn_resolve_splits(B, query_len, Hq, Hkv, D, page_size, bt_width,
+                                                window, num_splits))
+
+
+def workspace_size(B, query_len, Hq, Hkv, D, page_size, bt_width, window=0, num_splits=0) -> int:
+    return int(load().paged_attn_workspace_size(B, query_len, Hq, Hkv, D, page_size, bt_width,
+                                                window, num_splits))
+
+
+def paged_attn_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_table: torch.Tensor,
+                   seq_lens: torch.Tensor, *, scale: float, window: int = 0, num_splits: int = 0,
+                   k_scale: float = 1.0, v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+                   out_dtype: Optional[torch.dtype] = None, return_lse: bool = True,
+                   lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Attention of q [B, sq, Hq, D] over paged K/V views [pages, Hkv, P, D].
+
+    Returns (out [B, sq, Hq, D], lse [B, sq, Hq] fp32 natural log, or None)."""
+    B, sq, Hq, D = q.shape
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    desc = kv_desc(k, v, k_scale=k_scale, v_scale=v_scale)
+    if out is None:
+        out = torch.empty((B, sq, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, sq, Hq), dtype=torch.float32, device=q.device)
+    W = block_table.shape[1]
+    need = workspace_size(B, sq, Hq, desc.num_kv_heads, D, desc.page_size, W, window, num_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(load().paged_attn_run(
+        q.data_ptr(), dtype_code(q.dtype), ctypes.byref(desc), block_table.data_ptr(),
+        block_table.stride(0), W, seq_lens.data_ptr(), B, sq, Hq, D, float(scale), int(window),
+        int(num_splits), out.data_ptr(), dtype_code(out.dtype), _ptr(lse), _ptr(workspace), ws_bytes,
+        _stream(q.device)))
+    return out, lse
+
+
+def paged_attn_partial(q, k, v, block_table, seq_lens, *, scale: float, num_splits: int,
+                       window: int = 0, k_scale: float = 1.0, v_scale: float = 1.0,
+                       part_o: Optional[torch.Tensor] = None, part_lse: Optional[torch.Tensor] = None):
+    """Split-KV partials: (part_o [S, B*sq, Hq, D] fp32, part_lse [S, B*sq, Hq] fp32)."""
+    B, sq, Hq, D = q.shape
+    desc = kv_desc(k, v, k_scale=k_scale, v_scale=v_scale)
+    W = block_table.shape[1]
+    S = resolve_splits(B, sq, Hq, desc.num_kv_heads, D, desc.page_size, W, window, num_splits)
+    if part_o is None:
+        part_o = torch.empty((S, B * sq, Hq, D), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((S, B * sq, Hq), dtype=torch.float32, device=q.device)
+    check(load().paged_attn_partial(
+        q.data_ptr(), dtype_code(q.dtype), ctypes.byref(desc), block_table.data_ptr(),
+        block_table.stride(0), W, seq_lens.data_ptr(), B, sq, Hq, D, float(scale), int(window),
+        int(num_splits), part_o.data_ptr(), part_lse.data_ptr(), _stream(q.device)))
+    return part_o, part_lse
+
+
+def split_kv_combine(part_o: torch.Tensor, part_lse: torch.Tensor, *, out_dtype=torch.bfloat16,
+                     out: Optional[torch.Tensor] = None, return_lse: bool = True):
+    """LSE-weighted merge of Split-KV partials [S, rows, Hq, D] -> (out [rows, Hq, D], lse)."""
+    S, rows, Hq, D = part_o.shape
+    if out is None:
+        out = torch.empty((rows, Hq, D), dtype=out_dtype, device=part_o.device)
+    lse = torch.empty((rows, Hq), dtype=torch.float32, device=part_o.device) if return_lse else None
+    check(load().split_kv_combine(part_o.data_ptr(), part_lse.data_ptr(), S, rows, Hq, D,
+                                  out.data_ptr(), dtype_code(out.dtype), _ptr(lse),
+                                  _stream(part_o.device)))
+    return out, lse
+
+
+def segment_attn_combine(part_o: torch.Tensor, part_lse: torch.Tensor, used: torch.Tensor,
+                         bias: Optional[torch.Tensor], *, out_dtype=torch.bfloat16,
+                         out: Optional[torch.Tensor] = None, return_lse: bool = True):
+    """DASH combine of [N, G, Hq, D] partials with per-segment bias -> (out [N, Hq, D], lse)."""
+    N, G, Hq, D = part_o.shape
+    if out is None:
+        out = torch.empty((N, Hq, D), dtype=out_dtype, device=part_o.device)
+    lse = torch.empty((N, Hq), dtype=torch.float32, device=part_o.device) if return_lse else None
+    check(load().segment_attn_combine(part_o.data_ptr(), dtype_code(part_o.dtype),
+                                      part_lse.data_ptr(), used.data_ptr(), _ptr(bias), N, G, Hq, D,
+                                      out.data_ptr(), dtype_code(out.dtype), _ptr(lse),
+                                      _stream(part_o.device)))
+    return out, lse
+
+
+def segment_attn_workspace_size(N, topk, Hq, D) -> int:
+    return int(load().segment_attn_workspace_size(N, topk, Hq, D))
+
+
+def segment_attn_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, used: torch.Tensor,
+                     bias: torch.Tensor, *, bs: int, local: int, scale: Optional[float] = None,
+                     fused: bool = True, out_dtype: Optional[torch.dtype] = None,
+                     return_lse: bool = True, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """DASH attention of q [N, Hq, D] over gathered segments k, v [N*(topk*bs+local), Hkv, D]."""
+    N, Hq, D = q.shape
+    topk = bias.shape[1]
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty((N, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    if not fused and workspace is None:
+        workspace = torch.empty(segment_attn_workspace_size(N, topk, Hq, D), dtype=torch.uint8,
+                                device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(load().segment_attn_run(
+        q.data_ptr(), dtype_code(q.dtype), k.data_ptr(), v.data_ptr(), dtype_code(k.dtype),
+        used.data_ptr(), _ptr(bias), N, topk, int(bs), int(local), Hq, Hkv, D, float(scale),
+        1 if fused else 0, out.data_ptr(), dtype_code(out.dtype), _ptr(lse), _ptr(workspace),
+        ws_bytes, _stream(q.device)))
+    return out, lse
+
+
+def window_width(window: int, query_len: int, page_size: int, bt_width: int) -> int:
+    return int(load().paged_attn_window_width(window, query_len, page_size, bt_width))
+
+
+def _describe_shapes(block_table, query_len, Hq, Hkv, D, page_size, window, num_splits):
+    B, W = block_table.shape
+    S = resolve_splits(B, query_len, Hq, Hkv, D, page_size, W, window, num_splits)
+    ow = window_width(window, query_len, page_size, W)
+    return B, W, S, ow
+
+
+def paged_attn_describe(block_table, seq_lens, *, query_len, Hq, Hkv, D, page_size, window=0,
+                        num_splits=0):
+    """Device integer plan: (lens [B], table [B, width], split_ranges [B, S, 4]) int32."""
+    B, W, S, ow = _describe_shapes(block_table, query_len, Hq, Hkv, D, page_size, window, num_splits)
+    dev = block_table.device
+    lens = torch.empty(B, dtype=torch.int32, device=dev)
+    table = torch.empty((B, ow), dtype=torch.int32, device=dev)
+    ranges = torch.empty((B, S, 4), dtype=torch.int32, device=dev)
+    check(load().paged_attn_describe(block_table.data_ptr(), block_table.stride(0), W,
+                                     seq_lens.data_ptr(), B, query_len, Hq, Hkv, D, page_size,
+                                     window, num_splits, lens.data_ptr(), table.data_ptr(), ow,
+                                     ranges.data_ptr(), _stream(dev)))
+    return lens, table, ranges
+
+
+def paged_attn_describe_host(block_table, seq_lens, *, query_len, Hq, Hkv, D, page_size, window=0,
+                             num_splits=0):
+    """Same plan computed on the host from CPU int32 tensors (no GPU needed)."""
+    block_table = block_table.contiguous()
+    seq_lens = seq_lens.contiguous()
+    B, W, S, ow = _describe_shapes(block_table, query_len, Hq, Hkv, D, page_size, window, num_splits)
+    lens = torch.empty(B, dtype=torch.int32)
+    table = torch.empty((B, ow), dtype=torch.int32)
+    ranges = torch.empty((B, S, 4), dtype=torch.int32)
+    check(load().paged_attn_describe_host(block_table.data_ptr(), block_table.stride(0), W,
+                                          seq_lens.data_ptr(), B, query_len, Hq, Hkv, D, page_size,
+                                          window, num_splits, lens.data_ptr(), table.data_ptr(), ow,
+                                          ranges.data_ptr()))
+    return lens, table, ranges
+
+
+__all__ = [
+    "PagedAttnError", "dtype_code", "kv_desc", "kv_halves", "resolve_splits", "workspace_size",
+    "paged_attn_run", "paged_attn_partial", "split_kv_combine", "segment_attn_combine",
+    "segment_attn_run", "segment_attn_workspace_size", "window_width", "paged_attn_describe",
+    "paged_attn_describe_host",
+]
+PagedAttnError = _lib.PagedAttnError

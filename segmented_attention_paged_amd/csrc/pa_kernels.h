@@ -1,0 +1,66 @@
+// Kernel parameter blocks and host launchers shared by the HIP translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum Mode : int {
+  MODE_PAGED = 0,          // block-table addressed pages, optional window / Split-KV
+  MODE_SEGMENT = 1,        // one work item per (query, segment): partial O / LSE
+  MODE_SEGMENT_FUSED = 2,  // one work item per (query, kv head): bias folded, final O
+};
+
+struct AttnParams {
+  const void* q;        // [items, sq, Hq, D] (segment modes: [N, Hq, D])
+  const char* k;        // byte pointers to element 0 of K and V
+  const char* v;
+  int64_t page_stride;  // elements of the KV type
+  int64_t head_stride;
+  int64_t token_stride;
+  int32_t num_pages;
+  const int32_t* block_table;
+  int64_t bt_stride;
+  int32_t bt_width;
+  const int32_t* seq_lens;
+  int32_t items;        // paged: B; segment: N*(topk+1); fused: N
+  int32_t sq, Hq, Hkv, G, R, RG, P, window, S, chunk;
+  float qk_scale_log2;  // scale * k_scale * log2(e)
+  float v_scale;
+  void* out;            // final output (or partial O when S > 1 / segment mode)
+  int32_t out_kind;     // K_BF16 | K_FP16 | K_F32
+  float* lse;           // may be null unless partial
+  int64_t split_stride_o;    // elements between splits of part O (S > 1)
+  int64_t split_stride_lse;  // elements between splits of part LSE
+  int32_t partial;      // 1: write normalized fp32 partials, skip O of empty items
+  const int32_t* used;  // [N, topk+1]
+  const float* bias;    // [N, topk]
+  int32_t topk, bs, local;
+};
+
+struct LaunchShape {
+  int D, kv_kind, q_kind, RT, NW, mode;
+};
+
+hipError_t launch_attention(const AttnParams& p, const LaunchShape& s, int64_t grid,
+                            hipStream_t stream);
+
+bool attention_supported(const LaunchShape& s);
+
+hipError_t launch_split_combine(const float* part_o, const float* part_lse, int32_t S,
+                                int32_t rows, int32_t Hq, int32_t D, void* out, int32_t out_kind,
+                                float* lse, hipStream_t stream);
+
+hipError_t launch_segment_combine(const void* part_o, int32_t part_kind, const float* part_lse,
+                                  const int32_t* used, const float* bias, int32_t N, int32_t G,
+                                  int32_t Hq, int32_t D, void* out, int32_t out_kind, float* lse,
+                                  hipStream_t stream);
+
+hipError_t launch_describe(const int32_t* block_table, int64_t bt_stride, int32_t bt_width,
+                           const int32_t* seq_lens, int32_t B, int32_t query_len, int32_t P,
+                           int32_t window, int32_t S, int32_t chunk, int32_t* out_lens,
+                           int32_t* out_table, int32_t out_width, int32_t* split_ranges,
+                           hipStream_t stream);
+
+}  // namespace pa

@@ -31,6 +31,7 @@ import numpy as np
 import torch
 
 NAN_E4M3_BYTE = 0x7F  # e4m3fn encodes NaN as S.1111.111
+DEVICE_SEED_OFFSET = 7919  # seed offset of the on-device generator (large workloads)
 
 # Number of random values drawn per chunk when filling large buffers.  The
 # draw order (chunk by chunk along the leading dimension) is part of the recipe.
@@ -114,29 +115,34 @@ class SegmentInputs:
 
 
 def _randn_bf16(shape: Sequence[int], g: torch.Generator) -> torch.Tensor:
-    """N(0,1) fp32 draws rounded to bf16, drawn chunk by chunk along dim 0."""
-    out = torch.empty(tuple(shape), dtype=torch.bfloat16)
+    """N(0,1) fp32 draws rounded to bf16, drawn chunk by chunk along dim 0 on g's device."""
+    dev = g.device
+    out = torch.empty(tuple(shape), dtype=torch.bfloat16, device=dev)
     if out.numel() == 0:
         return out
     per_row = out[0].numel() if out.dim() > 0 else 1
     rows = max(1, _CHUNK_VALUES // max(per_row, 1))
     for r0 in range(0, out.shape[0], rows):
         r1 = min(out.shape[0], r0 + rows)
-        out[r0:r1] = torch.randn((r1 - r0,) + tuple(shape[1:]), generator=g).to(torch.bfloat16)
+        out[r0:r1] = torch.randn((r1 - r0,) + tuple(shape[1:]), generator=g, device=dev).to(torch.bfloat16)
     return out
 
 
 def _randn_e4m3_bytes(shape: Sequence[int], g: torch.Generator) -> torch.Tensor:
-    """e4m3fn(RNE(N(0,1))) stored as uint8 bytes, drawn chunk by chunk along dim 0."""
-    out = torch.empty(tuple(shape), dtype=torch.uint8)
+    """e4m3fn(RNE(N(0,1))) stored as uint8 bytes, drawn chunk by chunk along dim 0 on g's device."""
+    dev = g.device
+    out = torch.empty(tuple(shape), dtype=torch.uint8, device=dev)
     if out.numel() == 0:
         return out
     per_row = out[0].numel()
     rows = max(1, _CHUNK_VALUES // max(per_row, 1))
     for r0 in range(0, out.shape[0], rows):
         r1 = min(out.shape[0], r0 + rows)
-        x = torch.randn((r1 - r0,) + tuple(shape[1:]), generator=g)
-        out[r0:r1] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+        x = torch.randn((r1 - r0,) + tuple(shape[1:]), generator=g, device=dev)
+        try:
+            out[r0:r1] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+        except RuntimeError:  # no device-side fp8 cast: round on the host instead
+            out[r0:r1] = x.cpu().to(torch.float8_e4m3fn).view(torch.uint8).to(dev)
     return out
 
 
@@ -157,11 +163,15 @@ def make_paged(
     pool_pages: int = 0,
     table_width: int = 0,
     name: str = "paged",
+    device=None,
 ) -> PagedInputs:
     """Draw one paged-attention workload.
 
     ``seq_lens`` is either a sequence of ints or ``("uniform", lo, hi)`` for
-    lengths drawn uniformly from the integers in [lo, hi].
+    lengths drawn uniformly from the integers in [lo, hi].  With ``device``
+    set to a GPU, q and the cache are drawn there by a second generator
+    seeded with ``seed + DEVICE_SEED_OFFSET`` (same distributions, other
+    bytes; lengths, permutation and scales still come from the CPU stream).
     """
     if kv_dtype not in ("bf16", "fp8_e4m3"):
         raise ValueError(kv_dtype)
@@ -195,14 +205,15 @@ def make_paged(
         table[b, :n] = perm[cursor : cursor + n].to(torch.int32)
         cursor += n
 
-    # 3. queries
-    q = _randn_bf16((B, sq, Hq, D), g)
-
-    # 4. cache rows [K | V]
+    # 3. queries, 4. cache rows [K | V]
+    gd = g
+    if device is not None and torch.device(device).type != "cpu":
+        gd = torch.Generator(device=device).manual_seed(int(seed) + DEVICE_SEED_OFFSET)
+    q = _randn_bf16((B, sq, Hq, D), gd)
     if kv_dtype == "bf16":
-        cache = _randn_bf16((pool, Hkv, P, 2 * D), g)
+        cache = _randn_bf16((pool, Hkv, P, 2 * D), gd)
     else:
-        cache = _randn_e4m3_bytes((pool, Hkv, P, 2 * D), g)
+        cache = _randn_e4m3_bytes((pool, Hkv, P, 2 * D), gd)
 
     # 5. per-tensor fp8 scales
     if kv_dtype == "fp8_e4m3":
@@ -212,18 +223,19 @@ def make_paged(
         k_scale = v_scale = 1.0
 
     if poison:
-        nan = float("nan")
-        fill = (lambda t: t.fill_(nan)) if kv_dtype == "bf16" else (lambda t: t.fill_(NAN_E4M3_BYTE))
-        for p in spare.tolist():
-            fill(cache[p])
+        fill_value = float("nan") if kv_dtype == "bf16" else NAN_E4M3_BYTE
+        if spare.numel():
+            cache.index_fill_(0, spare.to(cache.device), fill_value)
         for b, (L, n) in enumerate(zip(lens_l, pages_per)):
             if n == 0:
                 continue
             last = int(table[b, n - 1])
             tail0 = L - (n - 1) * P
             if tail0 < P:
-                fill(cache[last, :, tail0:, :])
+                cache[last, :, tail0:, :] = fill_value
 
+    table = table.to(q.device)
+    lens = lens.to(q.device)
     return PagedInputs(
         name=name,
         B=B,
@@ -259,32 +271,41 @@ def make_segments(
     zero_frac: float = 0.1,
     poison: bool = False,
     name: str = "segments",
+    device=None,
 ) -> SegmentInputs:
     """Draw one DASH-style gathered-segment workload.
 
     used[n, g] is 0 with probability ``zero_frac``, otherwise uniform in
     {1..cap}, cap = bs for the topk remote segments and local for the last one.
+    With ``device`` set to a GPU, q, K and V are drawn there by a second
+    generator seeded with ``seed + DEVICE_SEED_OFFSET``.
     """
     g = torch.Generator().manual_seed(int(seed))
+    gd = g
+    if device is not None and torch.device(device).type != "cpu":
+        gd = torch.Generator(device=device).manual_seed(int(seed) + DEVICE_SEED_OFFSET)
     G = topk + 1
     T = N * (topk * bs + local)
-    q = _randn_bf16((N, Hq, D), g)
-    k = _randn_bf16((T, Hkv, D), g)
-    v = _randn_bf16((T, Hkv, D), g)
+    q = _randn_bf16((N, Hq, D), gd)
+    k = _randn_bf16((T, Hkv, D), gd)
+    v = _randn_bf16((T, Hkv, D), gd)
     zero = torch.rand((N, G), generator=g) < zero_frac
     caps = torch.tensor([bs] * topk + [local], dtype=torch.float64)
     u = torch.rand((N, G), generator=g, dtype=torch.float64)
     vals = torch.floor(u * caps).to(torch.int64) + 1  # uniform in {1..cap}
     used = torch.where(zero, torch.zeros_like(vals), vals).to(torch.int32)
     bias = torch.randn((N, topk), generator=g, dtype=torch.float32)
+    used = used.to(q.device)
+    bias = bias.to(q.device)
     if poison:
         per = topk * bs + local
         nan = float("nan")
+        used_host = used.cpu()
         for n in range(N):
             for s in range(G):
                 base = n * per + (s * bs if s < topk else topk * bs)
                 cap = bs if s < topk else local
-                u_ns = int(used[n, s])
+                u_ns = int(used_host[n, s])
                 if u_ns < cap:
                     k[base + u_ns : base + cap] = nan
                     v[base + u_ns : base + cap] = nan
@@ -339,18 +360,18 @@ CONFIGS = {
 }
 
 
-def paged_config(name: str, poison: bool = False) -> PagedInputs:
+def paged_config(name: str, poison: bool = False, device=None) -> PagedInputs:
     cfg = dict(CONFIGS[name])
     if cfg.pop("kind") != "paged":
         raise ValueError(name)
-    return make_paged(name=name, poison=poison, **cfg)
+    return make_paged(name=name, poison=poison, device=device, **cfg)
 
 
-def segment_config(name: str, poison: bool = False) -> SegmentInputs:
+def segment_config(name: str, poison: bool = False, device=None) -> SegmentInputs:
     cfg = dict(CONFIGS[name])
     if cfg.pop("kind") != "segments":
         raise ValueError(name)
-    return make_segments(name=name, poison=poison, **cfg)
+    return make_segments(name=name, poison=poison, device=device, **cfg)
 
 
 def to_numpy_bits(t: torch.Tensor) -> np.ndarray:
