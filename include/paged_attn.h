@@ -118,6 +118,16 @@ int32_t paged_attn_resolve_splits(int32_t B, int32_t query_len, int32_t Hq, int3
                                   int32_t D, int32_t page_size, int32_t bt_width,
                                   int32_t window, int32_t num_splits);
 
+/* The launch plan paged_attn_run uses for this shape, written to plan[0..5]:
+ * split count S, pages per split (0 = ceil(visible pages / S)), 16-row MFMA
+ * tiles per wave, waves per workgroup, row groups, workgroups in the grid.
+ * Passing -plan[1] (or plan[0] when plan[1] == 0) as num_splits to
+ * paged_attn_partial reproduces the partial pass of paged_attn_run.
+ * Host only; returns PA_EINVAL on a malformed shape. */
+int paged_attn_plan(int32_t B, int32_t query_len, int32_t Hq, int32_t Hkv, int32_t D,
+                    int32_t page_size, int32_t bt_width, int32_t window, int32_t num_splits,
+                    int32_t* plan);
+
 /* Bytes of workspace paged_attn_run needs for this shape (0 when one pass). */
 size_t paged_attn_workspace_size(int32_t B, int32_t query_len, int32_t Hq, int32_t Hkv,
                                  int32_t D, int32_t page_size, int32_t bt_width,

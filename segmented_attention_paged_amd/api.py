@@ -64,6 +64,16 @@ def resolve_splits(B, query_len, Hq, Hkv, D, page_size, bt_width, window=0, num_
                                                 window, num_splits))
 
 
+def plan(B, query_len, Hq, Hkv, D, page_size, bt_width, window=0, num_splits=0) -> dict:
+    """Launch plan of paged_attn_run for this shape (see paged_attn_plan in the header)."""
+    buf = (ctypes.c_int32 * 6)()
+    check(load().paged_attn_plan(B, query_len, Hq, Hkv, D, page_size, bt_width, window, num_splits,
+                                 buf))
+    S, chunk, rt, nw, rg, grid = list(buf)
+    return dict(splits=S, chunk_pages=chunk, row_tiles=rt, waves=nw, row_groups=rg, grid=grid,
+                partial_num_splits=(-chunk if chunk > 0 else S))
+
+
 def workspace_size(B, query_len, Hq, Hkv, D, page_size, bt_width, window=0, num_splits=0) -> int:
     return int(load().paged_attn_workspace_size(B, query_len, Hq, Hkv, D, page_size, bt_width,
                                                 window, num_splits))
@@ -220,7 +230,7 @@ def paged_attn_describe_host(block_table, seq_lens, *, query_len, Hq, Hkv, D, pa
 
 
 __all__ = [
-    "PagedAttnError", "dtype_code", "kv_desc", "kv_halves", "resolve_splits", "workspace_size",
+    "PagedAttnError", "dtype_code", "kv_desc", "kv_halves", "resolve_splits", "workspace_size", "plan",
     "paged_attn_run", "paged_attn_partial", "split_kv_combine", "segment_attn_combine",
     "segment_attn_run", "segment_attn_workspace_size", "window_width", "paged_attn_describe",
     "paged_attn_describe_host",

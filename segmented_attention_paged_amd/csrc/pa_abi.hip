@@ -3,6 +3,7 @@
 // synchronizes or reads device memory, so every entry point can be captured
 // into a hipGraph.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -172,6 +173,23 @@ int32_t paged_attn_resolve_splits(int32_t B, int32_t query_len, int32_t Hq, int3
   (void)D;
   if (Hkv <= 0 || Hq <= 0 || Hq % Hkv || page_size < 1 || bt_width < 1 || query_len < 1) return 1;
   return make_plan(B, query_len, Hq, Hkv, page_size, bt_width, window, num_splits).S;
+}
+
+int paged_attn_plan(int32_t B, int32_t query_len, int32_t Hq, int32_t Hkv, int32_t D,
+                    int32_t page_size, int32_t bt_width, int32_t window, int32_t num_splits,
+                    int32_t* plan) {
+  (void)D;
+  if (!plan) return fail(PA_EINVAL, "plan is NULL");
+  if (B < 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv || page_size < 1 || bt_width < 1 || query_len < 1)
+    return fail(PA_EINVAL, "bad plan geometry");
+  const Plan pl = make_plan(B, query_len, Hq, Hkv, page_size, bt_width, window, num_splits);
+  plan[0] = pl.S;
+  plan[1] = pl.chunk;
+  plan[2] = pl.RT;
+  plan[3] = pl.NW;
+  plan[4] = pl.RG;
+  plan[5] = (int32_t)std::min<int64_t>((int64_t)B * Hkv * pl.RG * pl.S, 0x7fffffff);
+  return ok();
 }
 
 size_t paged_attn_workspace_size(int32_t B, int32_t query_len, int32_t Hq, int32_t Hkv, int32_t D,
