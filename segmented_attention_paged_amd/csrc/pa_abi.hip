@@ -36,7 +36,7 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(PA_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int kTargetSlots = 8192;  // workgroup slots the automatic split aims for
+constexpr int64_t kTargetWorkgroups = 2048;  // workgroups the automatic split aims for
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
@@ -63,20 +63,17 @@ Plan make_plan(int32_t B, int32_t sq, int32_t Hq, int32_t Hkv, int32_t P, int32_
     pl.S = (int)std::max<int64_t>(1, cdiv(pages_max, pl.chunk));
     if (pl.S == 1) pl.chunk = 0;
   } else {
-    const int64_t tpp = cdiv(P, 16);
-    const int64_t tiles_max = (int64_t)pages_max * tpp;
+    // A few equal splits per request: enough workgroups to fill the chip, few
+    // enough that the per-workgroup start-up and the partial round trip stay
+    // small.  Single-wave workgroups (4 row tiles) want twice as many.
     const int64_t items = (int64_t)B * Hkv * pl.RG;
-    int64_t want = items * tiles_max / kTargetSlots;  // tiles per workgroup
-    int64_t ct = 8;
-    while (ct * 2 <= want && ct < 256) ct *= 2;
-    const int64_t chunk_pages = std::max<int64_t>(1, ct / tpp);
-    if (chunk_pages >= pages_max) {
-      pl.S = 1;
-      pl.chunk = 0;
-    } else {
-      pl.chunk = (int)chunk_pages;
-      pl.S = (int)cdiv(pages_max, chunk_pages);
-    }
+    const int64_t target = pl.NW == 1 ? 2 * kTargetWorkgroups : kTargetWorkgroups;
+    int64_t S = cdiv(target, std::max<int64_t>(items, 1));
+    const int64_t min_pages_per_split = std::max<int64_t>(1, cdiv(16, cdiv(P, 16)) );
+    S = std::min<int64_t>(S, std::max<int64_t>(1, pages_max / min_pages_per_split));
+    S = std::max<int64_t>(1, std::min<int64_t>(S, 64));
+    pl.S = (int)S;
+    pl.chunk = 0;
   }
   return pl;
 }
