@@ -115,7 +115,7 @@ class PagedBench:
         self.lse = torch.empty((inp.B, inp.sq, inp.Hq), dtype=torch.float32, device="cuda")
         ws = sap.workspace_size(inp.B, inp.sq, inp.Hq, inp.Hkv, inp.D, inp.P, W, inp.window,
                                 self.num_splits)
-        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
+        self.ws = sap.new_workspace(ws, "cuda")
         S = self.plan["splits"]
         self.part_o = torch.empty((S, inp.B * inp.sq, inp.Hq, inp.D), dtype=torch.float32,
                                   device="cuda")

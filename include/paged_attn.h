@@ -102,8 +102,11 @@ typedef struct pa_kv_desc {
  * out         [B, query_len, Hq, D], out_dtype PA_BF16 | PA_FP16 | PA_F32.
  * lse         [B, query_len, Hq] fp32 natural-log LSE, or NULL.
  * workspace   device scratch of >= paged_attn_workspace_size(...) bytes when
- *             the resolved split count exceeds 1 (else may be NULL); its
- *             contents need no initialization and are overwritten.
+ *             the resolved split count exceeds 1 (else may be NULL): the
+ *             fp32 partial outputs and LSEs of the splits, written by the
+ *             attention kernel and read by the combine kernel that follows it
+ *             on `stream`.  Its contents need no initialization; calls that
+ *             share a workspace must not overlap in time.
  * B == 0 or query_len == 0 is a no-op returning PA_OK.
  */
 int paged_attn_run(const void* q, int32_t q_dtype, const pa_kv_desc* kv,

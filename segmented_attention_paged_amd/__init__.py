@@ -23,5 +23,6 @@ from .api import (  # noqa: F401
     split_kv_combine,
     window_width,
     workspace_size,
+    new_workspace,
 )
 from ._lib import LIB_PATH, load  # noqa: F401

@@ -79,6 +79,11 @@ def workspace_size(B, query_len, Hq, Hkv, D, page_size, bt_width, window=0, num_
                                                 window, num_splits))
 
 
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A device workspace of at least nbytes (no initialization needed)."""
+    return torch.empty(((max(int(nbytes), 16) + 15) // 16) * 16, dtype=torch.uint8, device=device)
+
+
 def paged_attn_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_table: torch.Tensor,
                    seq_lens: torch.Tensor, *, scale: float, window: int = 0, num_splits: int = 0,
                    k_scale: float = 1.0, v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
@@ -100,7 +105,7 @@ def paged_attn_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_tabl
     W = block_table.shape[1]
     need = workspace_size(B, sq, Hq, desc.num_kv_heads, D, desc.page_size, W, window, num_splits)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = new_workspace(need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(load().paged_attn_run(
         q.data_ptr(), dtype_code(q.dtype), ctypes.byref(desc), block_table.data_ptr(),
@@ -231,6 +236,7 @@ def paged_attn_describe_host(block_table, seq_lens, *, query_len, Hq, Hkv, D, pa
 
 __all__ = [
     "PagedAttnError", "dtype_code", "kv_desc", "kv_halves", "resolve_splits", "workspace_size", "plan",
+    "new_workspace",
     "paged_attn_run", "paged_attn_partial", "split_kv_combine", "segment_attn_combine",
     "segment_attn_run", "segment_attn_workspace_size", "window_width", "paged_attn_describe",
     "paged_attn_describe_host",

@@ -44,16 +44,32 @@ int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 struct Plan {
   int RT, NW, RG;
   int S, chunk;
+  int rows_split;
 };
 
-Plan make_plan(int32_t B, int32_t sq, int32_t Hq, int32_t Hkv, int32_t P, int32_t bt_width,
-               int32_t window, int32_t num_splits) {
+// Up to 16 rows (decode): 4 waves split the keys of a work item.  More rows
+// (query blocks): one 16-row tile per wave, the waves sharing LDS-staged K/V
+// tiles; at most as many waves as a staged tile has 1 KiB loads for fp8 K/V
+// of this head_dim (so the plan does not depend on the cache dtype).
+Plan make_plan(int32_t B, int32_t sq, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+               int32_t bt_width, int32_t window, int32_t num_splits) {
   Plan pl{};
   const int G = Hq / Hkv;
   const int R = G * sq;
-  pl.RT = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
-  pl.NW = 4 / pl.RT;
-  pl.RG = (int)cdiv(R, 16 * pl.RT);
+  if (R <= 16) {
+    pl.rows_split = 0;
+    pl.RT = 1;
+    pl.NW = 4;
+    pl.RG = 1;
+  } else {
+    pl.rows_split = 1;
+    pl.RT = 1;
+    const int max_nw = std::min(8, shared_tile_loads(D, PA_FP8_E4M3));
+    int nw = 2;
+    while (nw < max_nw && 16 * nw < R) nw *= 2;
+    pl.NW = nw;
+    pl.RG = (int)cdiv(R, 16 * nw);
+  }
   const int32_t pages_max = pages_bound(window, sq, P, bt_width);
   if (num_splits > 0) {
     pl.S = num_splits;
@@ -65,10 +81,9 @@ Plan make_plan(int32_t B, int32_t sq, int32_t Hq, int32_t Hkv, int32_t P, int32_
   } else {
     // A few equal splits per request: enough workgroups to fill the chip, few
     // enough that the per-workgroup start-up and the partial round trip stay
-    // small.  Single-wave workgroups (4 row tiles) want twice as many.
+    // small.
     const int64_t items = (int64_t)B * Hkv * pl.RG;
-    const int64_t target = pl.NW == 1 ? 2 * kTargetWorkgroups : kTargetWorkgroups;
-    int64_t S = cdiv(target, std::max<int64_t>(items, 1));
+    int64_t S = cdiv(kTargetWorkgroups, std::max<int64_t>(items, 1));
     const int64_t min_pages_per_split = std::max<int64_t>(1, cdiv(16, cdiv(P, 16)) );
     S = std::min<int64_t>(S, std::max<int64_t>(1, pages_max / min_pages_per_split));
     S = std::max<int64_t>(1, std::min<int64_t>(S, 64));
@@ -167,19 +182,17 @@ int32_t paged_attn_window_width(int32_t window, int32_t query_len, int32_t page_
 int32_t paged_attn_resolve_splits(int32_t B, int32_t query_len, int32_t Hq, int32_t Hkv,
                                   int32_t D, int32_t page_size, int32_t bt_width, int32_t window,
                                   int32_t num_splits) {
-  (void)D;
   if (Hkv <= 0 || Hq <= 0 || Hq % Hkv || page_size < 1 || bt_width < 1 || query_len < 1) return 1;
-  return make_plan(B, query_len, Hq, Hkv, page_size, bt_width, window, num_splits).S;
+  return make_plan(B, query_len, Hq, Hkv, D, page_size, bt_width, window, num_splits).S;
 }
 
 int paged_attn_plan(int32_t B, int32_t query_len, int32_t Hq, int32_t Hkv, int32_t D,
                     int32_t page_size, int32_t bt_width, int32_t window, int32_t num_splits,
                     int32_t* plan) {
-  (void)D;
   if (!plan) return fail(PA_EINVAL, "plan is NULL");
   if (B < 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv || page_size < 1 || bt_width < 1 || query_len < 1)
     return fail(PA_EINVAL, "bad plan geometry");
-  const Plan pl = make_plan(B, query_len, Hq, Hkv, page_size, bt_width, window, num_splits);
+  const Plan pl = make_plan(B, query_len, Hq, Hkv, D, page_size, bt_width, window, num_splits);
   plan[0] = pl.S;
   plan[1] = pl.chunk;
   plan[2] = pl.RT;
@@ -199,6 +212,31 @@ size_t paged_attn_workspace_size(int32_t B, int32_t query_len, int32_t Hq, int32
   return (size_t)(align256((int64_t)S * rows * D * 4) + align256((int64_t)S * rows * 4));
 }
 
+// The partial pass of Split-KV (or the whole attention when S == 1 and `out`
+// is final) for one resolved plan.
+static int launch_paged(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
+                        const int32_t* block_table, int64_t bt_row_stride, int32_t bt_width,
+                        const int32_t* seq_lens, int32_t B, int32_t query_len, int32_t Hq,
+                        int32_t D, float scale, int32_t window, const Plan& pl, void* out,
+                        int32_t out_kind, float* lse, bool partial, hipStream_t stream) {
+  AttnParams p = paged_params(q, kv, block_table, bt_row_stride, bt_width, seq_lens, B, query_len,
+                              Hq, scale, window, pl);
+  const int64_t rows = (int64_t)B * query_len * Hq;
+  p.out = out;
+  p.out_kind = out_kind;
+  p.lse = lse;
+  p.partial = partial ? 1 : 0;
+  p.split_stride_o = rows * D;
+  p.split_stride_lse = rows;
+  LaunchShape ls{D, kv->dtype, q_dtype, pl.RT, pl.NW, MODE_PAGED, pl.rows_split};
+  if (pl.rows_split && (shared_tile_loads(D, kv->dtype) % pl.NW) != 0)
+    return fail(PA_ENOTSUP, "no shared-tile kernel for this head_dim / dtype / wave count");
+  const int64_t grid = (int64_t)B * kv->num_kv_heads * pl.RG * pl.S;
+  hipError_t e = launch_attention(p, ls, grid, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return PA_OK;
+}
+
 int paged_attn_partial(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
                        const int32_t* block_table, int64_t bt_row_stride, int32_t bt_width,
                        const int32_t* seq_lens, int32_t B, int32_t query_len, int32_t Hq, int32_t D,
@@ -210,22 +248,11 @@ int paged_attn_partial(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
   if (num_splits == 0) return fail(PA_EINVAL, "paged_attn_partial needs an explicit num_splits");
   if (B == 0 || query_len == 0) return ok();
   if (!part_o || !part_lse || !aligned16(part_o)) return fail(PA_EINVAL, "bad partial buffers");
-  const Plan pl = make_plan(B, query_len, Hq, kv->num_kv_heads, kv->page_size, bt_width, window,
+  const Plan pl = make_plan(B, query_len, Hq, kv->num_kv_heads, D, kv->page_size, bt_width, window,
                             num_splits);
-  AttnParams p = paged_params(q, kv, block_table, bt_row_stride, bt_width, seq_lens, B, query_len,
-                              Hq, scale, window, pl);
-  const int64_t rows = (int64_t)B * query_len * Hq;
-  p.out = part_o;
-  p.out_kind = PA_F32;
-  p.lse = part_lse;
-  p.partial = 1;
-  p.split_stride_o = rows * D;
-  p.split_stride_lse = rows;
-  const LaunchShape ls{D, kv->dtype, q_dtype, pl.RT, pl.NW, MODE_PAGED};
-  const int64_t grid = (int64_t)B * kv->num_kv_heads * pl.RG * pl.S;
-  hipError_t e = launch_attention(p, ls, grid, stream);
-  if (e != hipSuccess) return hip_fail(e, "attention launch");
-  return ok();
+  rc = launch_paged(q, q_dtype, kv, block_table, bt_row_stride, bt_width, seq_lens, B, query_len, Hq,
+                    D, scale, window, pl, part_o, PA_F32, part_lse, true, stream);
+  return rc == PA_OK ? ok() : rc;
 }
 
 int paged_attn_run(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
@@ -240,39 +267,26 @@ int paged_attn_run(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
     return fail(PA_ENOTSUP, "out dtype must be bf16, fp16 or f32 (got %d)", out_dtype);
   if (B == 0 || query_len == 0) return ok();
   if (!out || !aligned16(out)) return fail(PA_EINVAL, "out must be a 16-byte aligned pointer");
-  const Plan pl = make_plan(B, query_len, Hq, kv->num_kv_heads, kv->page_size, bt_width, window,
+  const Plan pl = make_plan(B, query_len, Hq, kv->num_kv_heads, D, kv->page_size, bt_width, window,
                             num_splits);
-  AttnParams p = paged_params(q, kv, block_table, bt_row_stride, bt_width, seq_lens, B, query_len,
-                              Hq, scale, window, pl);
-  const LaunchShape ls{D, kv->dtype, q_dtype, pl.RT, pl.NW, MODE_PAGED};
-  const int64_t grid = (int64_t)B * kv->num_kv_heads * pl.RG * pl.S;
-  const int64_t rows = (int64_t)B * query_len * Hq;
   if (pl.S == 1) {
-    p.out = out;
-    p.out_kind = out_dtype;
-    p.lse = lse;
-    p.partial = 0;
-    hipError_t e = launch_attention(p, ls, grid, stream);
-    if (e != hipSuccess) return hip_fail(e, "attention launch");
-    return ok();
+    rc = launch_paged(q, q_dtype, kv, block_table, bt_row_stride, bt_width, seq_lens, B, query_len,
+                      Hq, D, scale, window, pl, out, out_dtype, lse, false, stream);
+    return rc == PA_OK ? ok() : rc;
   }
   const size_t need = paged_attn_workspace_size(B, query_len, Hq, kv->num_kv_heads, D,
                                                 kv->page_size, bt_width, window, num_splits);
   if (!workspace || workspace_bytes < need || !aligned16(workspace))
     return fail(PA_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  const int64_t rows = (int64_t)B * query_len * Hq;
   float* part_o = static_cast<float*>(workspace);
   float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                              align256((int64_t)pl.S * rows * D * 4));
-  p.out = part_o;
-  p.out_kind = PA_F32;
-  p.lse = part_lse;
-  p.partial = 1;
-  p.split_stride_o = rows * D;
-  p.split_stride_lse = rows;
-  hipError_t e = launch_attention(p, ls, grid, stream);
-  if (e != hipSuccess) return hip_fail(e, "attention launch");
-  e = launch_split_combine(part_o, part_lse, pl.S, (int32_t)(B * query_len), Hq, D, out, out_dtype,
-                           lse, stream);
+  rc = launch_paged(q, q_dtype, kv, block_table, bt_row_stride, bt_width, seq_lens, B, query_len, Hq,
+                    D, scale, window, pl, part_o, PA_F32, part_lse, true, stream);
+  if (rc != PA_OK) return rc;
+  hipError_t e = launch_split_combine(part_o, part_lse, pl.S, (int32_t)(B * query_len), Hq, D, out,
+                                      out_dtype, lse, stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ok();
 }
@@ -367,7 +381,7 @@ int segment_attn_run(const void* q, int32_t q_dtype, const void* k, const void* 
     p.out_kind = out_dtype;
     p.lse = lse;
     p.partial = 0;
-    const LaunchShape ls{D, kv_dtype, q_dtype, RT, NW, MODE_SEGMENT_FUSED};
+    const LaunchShape ls{D, kv_dtype, q_dtype, RT, NW, MODE_SEGMENT_FUSED, 0};
     hipError_t e = launch_attention(p, ls, (int64_t)N * Hkv * RG, stream);
     if (e != hipSuccess) return hip_fail(e, "segment attention launch");
     return ok();
@@ -385,7 +399,7 @@ int segment_attn_run(const void* q, int32_t q_dtype, const void* k, const void* 
   p.out_kind = PA_F32;
   p.lse = part_lse;
   p.partial = 1;
-  const LaunchShape ls{D, kv_dtype, q_dtype, RT, NW, MODE_SEGMENT};
+  const LaunchShape ls{D, kv_dtype, q_dtype, RT, NW, MODE_SEGMENT, 0};
   hipError_t e = launch_attention(p, ls, (int64_t)N * Gs * Hkv * RG, stream);
   if (e != hipSuccess) return hip_fail(e, "segment attention launch");
   e = launch_segment_combine(part_o, PA_F32, part_lse, used, bias, N, Gs, Hq, D, out, out_dtype,
@@ -412,7 +426,7 @@ int paged_attn_describe(const int32_t* block_table, int64_t bt_row_stride, int32
   if (rc != PA_OK) return rc;
   if (B == 0) return ok();
   if (!block_table || !seq_lens || !out_lens) return fail(PA_EINVAL, "NULL pointer");
-  const Plan pl = make_plan(B, query_len, Hq, Hkv, page_size, bt_width, window, num_splits);
+  const Plan pl = make_plan(B, query_len, Hq, Hkv, D, page_size, bt_width, window, num_splits);
   hipError_t e = launch_describe(block_table, bt_row_stride, bt_width, seq_lens, B, query_len,
                                  page_size, window > 0 ? window : 0, pl.S, pl.chunk, out_lens,
                                  out_table, out_width, split_ranges, stream);
@@ -430,7 +444,7 @@ int paged_attn_describe_host(const int32_t* block_table, int64_t bt_row_stride, 
   if (rc != PA_OK) return rc;
   if (B == 0) return ok();
   if (!block_table || !seq_lens || !out_lens) return fail(PA_EINVAL, "NULL pointer");
-  const Plan pl = make_plan(B, query_len, Hq, Hkv, page_size, bt_width, window, num_splits);
+  const Plan pl = make_plan(B, query_len, Hq, Hkv, D, page_size, bt_width, window, num_splits);
   const int32_t w = window > 0 ? window : 0;
   for (int b = 0; b < B; ++b) {
     const SeqView sv = seq_view(seq_lens[b], w, query_len, page_size, bt_width);

@@ -1,28 +1,34 @@
-// Paged / segmented attention kernel for gfx950 (CDNA4, wave64, MFMA).
+// Paged / segmented attention kernels for gfx950 (CDNA4, wave64, MFMA).
 //
-// One workgroup = NW waves = one work item:
-//   paged:          (request, kv head, row group, split)
-//   segment:        (query, segment, kv head, row group)
-//   segment fused:  (query, kv head, row group)
-// The rows of a work item are the G query heads of one kv head times the
-// query block (row r -> token r / G, head kvh*G + r % G), packed into 16-row
-// MFMA tiles (RT tiles per wave).  Keys are consumed in tiles of 16 slots of
-// one page.  Waves of a workgroup take tiles round-robin, each keeping its
-// own online-softmax state; the states are merged through LDS at the end.
+// Rows of a work item are the G query heads of one kv head times the query
+// block (row r -> token r / G, head kvh*G + r % G), packed into 16-row MFMA
+// tiles.  Keys are consumed in tiles of 16 slots of one page.
 //
 // Per 16-key tile and 16-row tile:
-//   S^T = K Q^T   D/32  x v_mfma_f32_16x16x32_{bf16,f16}; K is the A operand,
-//                 loaded straight from the page: lane l reads 16 contiguous
-//                 bytes of key l%16 (no LDS, no shuffles).
-//   online softmax in fp32 registers (log2 domain, v_exp_f32).
-//   O^T += V^T P^T  D/16 x v_mfma_f32_16x16x16_{bf16,f16}; P^T is the S^T
-//                 accumulator re-packed to 16 bits in place (same lane layout),
-//                 V^T is built from 4 keys x 16 bytes per lane with byte
-//                 permutes: A-row m of MFMA j is head-dim VPL*m + j.
+//   S^T = K Q^T      D/32 x v_mfma_f32_16x16x32_{bf16,f16}; K is the A operand
+//                    (lane l: key l%16, 16 contiguous bytes of its row).
+//   online softmax   fp32 registers, log2 domain, v_exp_f32.
+//   O^T += V^T P^T   D/16 x v_mfma_f32_16x16x16_{bf16,f16}; P^T is the S^T
+//                    accumulator re-packed to 16 bits in place (same lane
+//                    layout); V^T comes from 4 keys x VPL head-dim values per
+//                    lane with 16-bit permutes: A-row m of MFMA j is head-dim
+//                    VPL*m + j.
 // fp8 (e4m3fn) K/V are decoded exactly to the query's 16-bit type with the
 // gfx950 pk conversions; k_scale folds into the logit scale and v_scale into
 // the epilogue (vllm.v1.attention.backends.flashinfer_ts, forward:
 // bmm1_scale / bmm2_scale).
+//
+// Two kernels:
+//   attn_kernel         waves of a workgroup split the KEYS (round-robin
+//                       tiles, K/V loaded straight into registers one tile
+//                       ahead) and merge their softmax states through LDS.
+//                       Used for <= 16 rows (decode) and the segment modes.
+//   attn_shared_kernel  waves split the ROWS (one 16-row tile each) and all
+//                       consume the same K/V tiles, which stream through an
+//                       NBUF-stage LDS ring filled by direct-to-LDS loads
+//                       (global_load_lds_dwordx4): one HBM read per tile, no
+//                       VGPR staging, NBUF-1 tiles in flight.  Used for query
+//                       blocks with more than 16 rows.
 
 #include "pa_device.h"
 #include "pa_kernels.h"
@@ -34,6 +40,21 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+template <int D, int KV>
+struct Geo {
+  static constexpr int KB = (KV == K_FP8) ? 1 : 2;  // bytes per stored K/V element
+  static constexpr int NKC = D / 32;                // QK MFMAs per row tile
+  static constexpr int VPL = D / 16;                // PV MFMAs per row tile
+  static constexpr int KLD = D * KB / 64;           // 16-byte K pieces per lane per tile
+  static constexpr int VB = VPL * KB;               // V bytes per lane per key
+  static constexpr int VDW = VB / 4;                // ... in dwords
+  static constexpr int RB = 2 * D * KB;             // bytes of one key's K and V in a staged tile
+  static constexpr int CPK = RB / 16;               // 16-byte chunks per staged key
+  static constexpr int SWZ = CPK / 2 - 1;           // chunk swizzle mask (stays inside K or V)
+  static constexpr int TILE_BYTES = 16 * RB;
+  static constexpr int IPT = TILE_BYTES / 1024;     // 1 KiB direct-to-LDS loads per tile
+};
+
 struct TileInfo {
   const char* kp;  // byte address of slot 0 of the tile, head kvh, in K
   const char* vp;  // same in V
@@ -41,8 +62,27 @@ struct TileInfo {
   float bias;      // log2-domain logit bias of the tile (fused segments)
 };
 
+// K/V bytes are read exactly once per launch: non-temporal loads keep them
+// from displacing anything in the caches (measured +14% on random 8 KiB pages).
+__device__ __forceinline__ u32x4 stream_load16(const char* src) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+}
+
 template <int VDW>
 __device__ __forceinline__ void load_v(uint32_t (&dst)[VDW], const char* src) {
+  if constexpr (VDW == 4) {
+    const u32x4 x = stream_load16(src);
+    dst[0] = x[0]; dst[1] = x[1]; dst[2] = x[2]; dst[3] = x[3];
+  } else if constexpr (VDW == 2) {
+    const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
+    dst[0] = x[0]; dst[1] = x[1];
+  } else {
+    dst[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src));
+  }
+}
+
+template <int VDW>
+__device__ __forceinline__ void lds_read_v(uint32_t (&dst)[VDW], const char* src) {
   if constexpr (VDW == 4) {
     const u32x4 x = *reinterpret_cast<const u32x4*>(src);
     dst[0] = x[0]; dst[1] = x[1]; dst[2] = x[2]; dst[3] = x[3];
@@ -54,61 +94,226 @@ __device__ __forceinline__ void load_v(uint32_t (&dst)[VDW], const char* src) {
   }
 }
 
+// Raw K/V bytes of one tile as one lane holds them: K pieces of key l%16 and
+// the V values of keys 4*(l/16)+i.
+template <int D, int KV>
+struct Raw {
+  u32x4 k[Geo<D, KV>::KLD];
+  uint32_t v[4][Geo<D, KV>::VDW];
+};
+
+// MFMA operands of one tile in the query's 16-bit type.
+template <int D>
+struct Frags {
+  u32x4 kf[D / 32];
+  u32x2 vA[D / 16];
+};
+
+template <int D, int KV, int QT>
+__device__ __forceinline__ void make_frags(const Raw<D, KV>& r, Frags<D>& f) {
+  using G = Geo<D, KV>;
+  if constexpr (KV == K_FP8) {
+#pragma unroll
+    for (int c2 = 0; c2 < G::KLD; ++c2) {
+      uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
+      fp8x4_to_16<QT>(r.k[c2][0], a0, a1);
+      fp8x4_to_16<QT>(r.k[c2][1], a2, a3);
+      fp8x4_to_16<QT>(r.k[c2][2], b0, b1);
+      fp8x4_to_16<QT>(r.k[c2][3], b2, b3);
+      f.kf[2 * c2] = u32x4{a0, a1, a2, a3};
+      f.kf[2 * c2 + 1] = u32x4{b0, b1, b2, b3};
+    }
+  } else {
+#pragma unroll
+    for (int kc = 0; kc < G::NKC; ++kc) f.kf[kc] = r.k[kc];
+  }
+  uint32_t v16[4][G::VPL / 2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (KV == K_FP8) {
+#pragma unroll
+      for (int w = 0; w < G::VDW; ++w) fp8x4_to_16<QT>(r.v[i][w], v16[i][2 * w], v16[i][2 * w + 1]);
+    } else {
+#pragma unroll
+      for (int w = 0; w < G::VDW; ++w) v16[i][w] = r.v[i][w];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < G::VPL; ++j) {
+    const int w = j >> 1;
+    if ((j & 1) == 0)
+      f.vA[j] = u32x2{lo_lo(v16[0][w], v16[1][w]), lo_lo(v16[2][w], v16[3][w])};
+    else
+      f.vA[j] = u32x2{hi_hi(v16[0][w], v16[1][w]), hi_hi(v16[2][w], v16[3][w])};
+  }
+}
+
+// Query fragments (B operand of S^T = K Q^T) for row tile starting at `row0`.
+template <int D, int KV>
+__device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const void* q, int row0, int R, int G,
+                                       int kvh, int qb, int sq, int Hq, int g4, int c16) {
+  const int rr = row0 + c16;
+  if (rr < R) {
+    const int t = rr / G, gg = rr % G;
+    const int h = kvh * G + gg;
+    const uint16_t* qrow =
+        reinterpret_cast<const uint16_t*>(q) + (((int64_t)qb * sq + t) * Hq + h) * D;
+#pragma unroll
+    for (int kc = 0; kc < D / 32; ++kc) {
+      const int d = (KV == K_FP8) ? 64 * (kc >> 1) + 16 * g4 + 8 * (kc & 1) : 32 * kc + 8 * g4;
+      qf[kc] = *reinterpret_cast<const u32x4*>(qrow + d);
+    }
+  } else {
+#pragma unroll
+    for (int kc = 0; kc < D / 32; ++kc) qf[kc] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// One 16-key tile against one 16-row tile: S^T, online softmax, O^T += V^T P^T.
+template <int D, int QT>
+__device__ __forceinline__ void attend_tile(const Frags<D>& f, const u32x4 (&qf)[D / 32],
+                                            f32x4 (&acc)[D / 16], float& m_run, float& l_run,
+                                            float scale_log2, float bias, int nvalid, int g4) {
+  f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kc = 0; kc < D / 32; ++kc) sacc = mfma_16x16x32<QT>(f.kf[kc], qf[kc], sacc);
+  float s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = sacc[i] * scale_log2 + bias;
+  if (nvalid < 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * g4 + i >= nvalid) s[i] = kNegInf;
+  }
+  float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  tmax = max_across_groups(tmax);
+  const float m_new = fmaxf(m_run, tmax);
+  const float alpha = fast_exp2(m_run - m_new);
+  float pr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s[i] - m_new);
+  l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+  m_run = m_new;
+  const u32x2 pB = u32x2{pack2<QT>(pr[0], pr[1]), pack2<QT>(pr[2], pr[3])};
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    acc[j] *= alpha;
+    acc[j] = mfma_16x16x16<QT>(f.vA[j], pB, acc[j]);
+  }
+}
+
+// Write one lane's part of a finished 16-row tile: row row0 + l%16, head-dim
+// values VPL*(4*(l/16)+i) + j = acc[j][i] / l (times v_scale).  Partial
+// outputs (fp32) of rows that saw no key are skipped; their LSE is -inf.
+template <int D>
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[D / 16], float m_run, float l_run,
+                                           float v_scale, void* out, int out_kind, float* lse,
+                                           int64_t orow, bool partial, int g4) {
+  constexpr int VPL = D / 16;
+  const bool live = l_run > 0.f;
+  const float inv = live ? v_scale / l_run : 0.f;
+  if (live || !partial) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float vals[VPL];
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) vals[j] = acc[j][i] * inv;
+      store_row<VPL>(out, orow * D + VPL * (4 * g4 + i), out_kind, vals);
+    }
+  }
+  if (g4 == 0 && lse) lse[orow] = live ? (m_run + log2f(l_run)) * kLn2 : kNegInf;
+}
+
+// Pages / tiles of one (request, split) of the paged mode.
+struct PagedRange {
+  SeqView sv;
+  SplitRange sr;
+  int TPP;      // 16-slot tiles per page
+  int tok_end;  // first invisible key of the split (restricted numbering)
+  int n_tiles;
+};
+
+__device__ __forceinline__ PagedRange paged_range(const AttnParams& p, int item, int split) {
+  PagedRange r;
+  r.sv = seq_view(p.seq_lens[item], p.window, p.sq, p.P, p.bt_width);
+  r.sr = split_range(r.sv, p.P, p.S, p.chunk, split);
+  r.TPP = (p.P + 15) >> 4;
+  r.tok_end = r.sr.tok0 + r.sr.n_tok;
+  r.n_tiles = 0;
+  if (r.sr.n_pages > 0) {
+    const int last_count = r.sr.n_tok - (r.sr.n_pages - 1) * p.P;
+    r.n_tiles = (r.sr.n_pages - 1) * r.TPP + ((last_count + 15) >> 4);
+  }
+  return r;
+}
+
+// Tile `it` of a paged split: page, first slot and number of visible slots.
+__device__ __forceinline__ void paged_tile(const AttnParams& p, const PagedRange& r, int it,
+                                           int& page, int& slot0, int& nvalid) {
+  const int pin = it / r.TPP, u = it - pin * r.TPP;
+  page = r.sr.first_page + pin;
+  slot0 = 16 * u;
+  const int tok0 = page * p.P + slot0;
+  int nv = p.P - slot0;
+  if (nv > 16) nv = 16;
+  if (r.tok_end - tok0 < nv) nv = r.tok_end - tok0;
+  nvalid = nv;
+}
+
+// Pool page of restricted page `page`, clamped into the pool.
+__device__ __forceinline__ int32_t load_phys(const AttnParams& p, const int32_t* trow,
+                                             const SeqView& sv, int page) {
+  int32_t ph = trow[table_column(sv, page, p.bt_width)];
+  return ph < 0 ? 0 : (ph >= p.num_pages ? p.num_pages - 1 : ph);
+}
+
 }  // namespace
 
+// ================================================================================
+// attn_kernel: waves split the keys of a work item.
+//   paged:          work item (request, kv head, row group, split)
+//   segment:        (query, segment, kv head, row group)
+//   segment fused:  (query, kv head, row group); segment g's logits get its bias
+// ================================================================================
 template <int D, int RT, int NW, int KV, int QT, int MODE>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
-  static_assert(D == 64 || D == 128, "head_dim");
-  constexpr int KB = (KV == K_FP8) ? 1 : 2;  // bytes per stored K/V element
-  constexpr int NKC = D / 32;                // QK MFMAs per row tile
-  constexpr int VPL = D / 16;                // PV MFMAs per row tile = head-dim values per lane per key
-  constexpr int KLD = D * KB / 64;           // 16-byte K loads per lane per tile
-  constexpr int VDW = VPL * KB / 4;          // V dwords per lane per key
+  using G = Geo<D, KV>;
+  constexpr int KB = G::KB;
+  constexpr int VPL = G::VPL;
   constexpr int ROWS = RT * 16;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g4 = lane >> 4;
   const int c16 = lane & 15;
 
-  // ---- work item ------------------------------------------------------------
-  int64_t bid = blockIdx.x;
+  uint32_t bid = blockIdx.x;  // 32-bit: the grid never exceeds 2^31 workgroups
   int split = 0;
   if constexpr (MODE == MODE_PAGED) {
-    split = (int)(bid % p.S);
-    bid /= p.S;
+    split = (int)(bid % (uint32_t)p.S);
+    bid /= (uint32_t)p.S;
   }
-  const int rg = (int)(bid % p.RG);
-  bid /= p.RG;
-  const int kvh = (int)(bid % p.Hkv);
-  const int item = (int)(bid / p.Hkv);
+  const int rg = (int)(bid % (uint32_t)p.RG);
+  bid /= (uint32_t)p.RG;
+  const int kvh = (int)(bid % (uint32_t)p.Hkv);
+  const int item = (int)(bid / (uint32_t)p.Hkv);
 
   const int64_t ts_b = p.token_stride * KB;
   const int64_t head_off_b = (int64_t)kvh * p.head_stride * KB;
 
   int n_tiles = 0;
-  int qb = item;  // request index used to address q and the output rows
-  // paged
-  SeqView sv{};
-  SplitRange sr{};
-  int TPP = 1, tok_end = 0;
-  // segment
+  int qb = item;  // query row block
+  PagedRange pr{};
   int64_t seg_tok0 = 0;
   int seg_used = 0;
-  // fused segments: lane g holds the description of segment g
+  // fused segments: lane g describes segment g
   int f_used = 0, f_tiles = 0, f_cum_end = 0x7fffffff;
   int64_t f_base = 0;
   float f_bias = 0.f;
 
   if constexpr (MODE == MODE_PAGED) {
-    sv = seq_view(p.seq_lens[item], p.window, p.sq, p.P, p.bt_width);
-    sr = split_range(sv, p.P, p.S, p.chunk, split);
-    TPP = (p.P + 15) >> 4;
-    tok_end = sr.tok0 + sr.n_tok;
-    if (sr.n_pages > 0) {
-      const int last_count = sr.n_tok - (sr.n_pages - 1) * p.P;
-      n_tiles = (sr.n_pages - 1) * TPP + ((last_count + 15) >> 4);
-    }
+    pr = paged_range(p, item, split);
+    n_tiles = pr.n_tiles;
   } else if constexpr (MODE == MODE_SEGMENT) {
     const int Gs = p.topk + 1;
     const int n = item / Gs, gs = item % Gs;
@@ -131,8 +336,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
       f_base = (int64_t)n * (p.topk * p.bs + p.local) + (lane < p.topk ? lane * p.bs : p.topk * p.bs);
       f_bias = lane < p.topk ? p.bias[(int64_t)n * p.topk + lane] * kLog2e : 0.f;
     }
-    // inclusive prefix sum of tile counts across lanes
-    int cum = f_tiles;
+    int cum = f_tiles;  // inclusive prefix sum of tile counts across lanes
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int o = __shfl_up(cum, off, 64);
@@ -143,30 +347,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
     qb = n;
   }
 
-  // ---- query fragments (B operand of S^T = K Q^T) -----------------------------
-  u32x4 qf[RT][NKC];
   const int row_base = rg * ROWS;
+  u32x4 qf[RT][D / 32];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int rr = row_base + rt * 16 + c16;
-    if (rr < p.R) {
-      const int t = rr / p.G, gg = rr % p.G;
-      const int h = kvh * p.G + gg;
-      const uint16_t* qrow =
-          reinterpret_cast<const uint16_t*>(p.q) + (((int64_t)qb * p.sq + t) * p.Hq + h) * D;
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const int d = (KV == K_FP8) ? 64 * (kc >> 1) + 16 * g4 + 8 * (kc & 1) : 32 * kc + 8 * g4;
-        qf[rt][kc] = *reinterpret_cast<const u32x4*>(qrow + d);
-      }
-    } else {
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) qf[rt][kc] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
+  for (int rt = 0; rt < RT; ++rt)
+    load_q<D, KV>(qf[rt], p.q, row_base + rt * 16, p.R, p.G, kvh, qb, p.sq, p.Hq, g4, c16);
 
-  // ---- per-wave page index cache (paged): lane i holds the pool page of the
-  // wave's tile k0 + i ---------------------------------------------------------
+  // paged: lane i caches the pool page of the wave's tile k0 + i
   int32_t phys_vec = 0;
   int k0 = -64;
   const int32_t* trow = nullptr;
@@ -181,34 +368,25 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
         k0 = k;
         const int itl = wave + NW * (k0 + lane);
         int32_t ph = 0;
-        if (itl < n_tiles) {
-          const int page = sr.first_page + itl / TPP;
-          ph = trow[table_column(sv, page, p.bt_width)];
-          ph = ph < 0 ? 0 : (ph >= p.num_pages ? p.num_pages - 1 : ph);
-        }
+        if (itl < n_tiles) ph = load_phys(p, trow, pr.sv, pr.sr.first_page + itl / pr.TPP);
         phys_vec = ph;
       }
       const int32_t phys = __builtin_amdgcn_readlane(phys_vec, k - k0);
-      const int pin = it / TPP, u = it - pin * TPP;
-      const int page = sr.first_page + pin;
-      const int slot0 = 16 * u;
-      const int tok0 = page * p.P + slot0;
-      int nv = p.P - slot0;
-      if (nv > 16) nv = 16;
-      if (tok_end - tok0 < nv) nv = tok_end - tok0;
+      int page, slot0, nv;
+      paged_tile(p, pr, it, page, slot0, nv);
       ti.nvalid = nv;
       const int64_t off = ((int64_t)phys * p.page_stride + (int64_t)slot0 * p.token_stride) * KB + head_off_b;
       ti.kp = p.k + off;
       ti.vp = p.v + off;
     } else if constexpr (MODE == MODE_SEGMENT) {
       const int64_t tok = seg_tok0 + 16 * it;
-      int nv = seg_used - 16 * it;
+      const int nv = seg_used - 16 * it;
       ti.nvalid = nv > 16 ? 16 : nv;
       const int64_t off = tok * ts_b + head_off_b;
       ti.kp = p.k + off;
       ti.vp = p.v + off;
     } else {
-      // segment holding tile `it`: number of segments that end at or before it
+      // segment holding tile `it`: the number of segments that end at or before it
       const int gsel = __builtin_popcountll(__ballot(f_cum_end <= it));
       const int cend = __shfl(f_cum_end, gsel, 64);
       const int ntl = __shfl(f_tiles, gsel, 64);
@@ -216,7 +394,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
       const int64_t base = __shfl(f_base, gsel, 64);
       ti.bias = __shfl(f_bias, gsel, 64);
       const int lt = it - (cend - ntl);
-      int nv = ul - 16 * lt;
+      const int nv = ul - 16 * lt;
       ti.nvalid = nv > 16 ? 16 : nv;
       const int64_t off = (base + 16 * lt) * ts_b + head_off_b;
       ti.kp = p.k + off;
@@ -225,20 +403,16 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
     return ti;
   };
 
-  struct Raw {
-    u32x4 k[KLD];
-    uint32_t v[4][VDW];
-  };
-  auto load_tile = [&](Raw& r, const TileInfo& ti) {
-    const int ks = c16 < ti.nvalid ? c16 : 0;  // invalid slots read slot 0 (masked below)
+  auto load_tile = [&](Raw<D, KV>& r, const TileInfo& ti) {
+    const int ks = c16 < ti.nvalid ? c16 : 0;  // invalid slots read slot 0 (masked later)
     const char* kl = ti.kp + ks * ts_b + 16 * g4;
 #pragma unroll
-    for (int i = 0; i < KLD; ++i) r.k[i] = *reinterpret_cast<const u32x4*>(kl + 64 * i);
+    for (int i = 0; i < G::KLD; ++i) r.k[i] = stream_load16(kl + 64 * i);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int vs = 4 * g4 + i;
       vs = vs < ti.nvalid ? vs : 0;
-      load_v<VDW>(r.v[i], ti.vp + vs * ts_b + VPL * KB * c16);
+      load_v<G::VDW>(r.v[i], ti.vp + vs * ts_b + G::VB * c16);
     }
   };
 
@@ -252,91 +426,25 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
     for (int j = 0; j < VPL; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto compute_tile = [&](const Raw& r, const TileInfo& ti) {
-    // K fragments in the query's 16-bit type
-    u32x4 kf[NKC];
-    if constexpr (KV == K_FP8) {
-#pragma unroll
-      for (int c2 = 0; c2 < KLD; ++c2) {
-        uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
-        fp8x4_to_16<QT>(r.k[c2][0], a0, a1);
-        fp8x4_to_16<QT>(r.k[c2][1], a2, a3);
-        fp8x4_to_16<QT>(r.k[c2][2], b0, b1);
-        fp8x4_to_16<QT>(r.k[c2][3], b2, b3);
-        kf[2 * c2] = u32x4{a0, a1, a2, a3};
-        kf[2 * c2 + 1] = u32x4{b0, b1, b2, b3};
-      }
-    } else {
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) kf[kc] = r.k[kc];
-    }
-    // V^T fragments: vA[j] holds head-dim VPL*c16 + j of keys 4*g4 + 0..3
-    uint32_t v16[4][VPL / 2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (KV == K_FP8) {
-#pragma unroll
-        for (int w = 0; w < VDW; ++w) fp8x4_to_16<QT>(r.v[i][w], v16[i][2 * w], v16[i][2 * w + 1]);
-      } else {
-#pragma unroll
-        for (int w = 0; w < VDW; ++w) v16[i][w] = r.v[i][w];
-      }
-    }
-    u32x2 vA[VPL];
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const int w = j >> 1;
-      if ((j & 1) == 0)
-        vA[j] = u32x2{lo_lo(v16[0][w], v16[1][w]), lo_lo(v16[2][w], v16[3][w])};
-      else
-        vA[j] = u32x2{hi_hi(v16[0][w], v16[1][w]), hi_hi(v16[2][w], v16[3][w])};
-    }
-    const bool partial_tile = ti.nvalid < 16;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) sacc = mfma_16x16x32<QT>(kf[kc], qf[rt][kc], sacc);
-      float s[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = sacc[i] * p.qk_scale_log2 + ti.bias;
-      if (partial_tile) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * g4 + i >= ti.nvalid) s[i] = kNegInf;
-      }
-      float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      tmax = max_across_groups(tmax);
-      const float m_new = fmaxf(m_run[rt], tmax);
-      const float alpha = fast_exp2(m_run[rt] - m_new);
-      float pr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s[i] - m_new);
-      l_run[rt] = l_run[rt] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-      m_run[rt] = m_new;
-      const u32x2 pB = u32x2{pack2<QT>(pr[0], pr[1]), pack2<QT>(pr[2], pr[3])};
-#pragma unroll
-      for (int j = 0; j < VPL; ++j) {
-        acc[rt][j] *= alpha;
-        acc[rt][j] = mfma_16x16x16<QT>(vA[j], pB, acc[rt][j]);
-      }
-    }
-  };
-
-  // ---- main loop: prefetch tile k+1 while computing tile k --------------------
+  // main loop: tile k+1 is in flight while tile k is computed
   if (wave < n_tiles) {
     TileInfo ti = tile_info(0);
-    Raw cur;
+    Raw<D, KV> cur;
     load_tile(cur, ti);
     for (int k = 0;; ++k) {
       const bool more = wave + NW * (k + 1) < n_tiles;
       TileInfo tn = ti;
-      Raw nxt;
+      Raw<D, KV> nxt;
       if (more) {
         tn = tile_info(k + 1);
         load_tile(nxt, tn);
       }
-      compute_tile(cur, ti);
+      Frags<D> f;
+      make_frags<D, KV, QT>(cur, f);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        attend_tile<D, QT>(f, qf[rt], acc[rt], m_run[rt], l_run[rt], p.qk_scale_log2, ti.bias,
+                           ti.nvalid, g4);
       if (!more) break;
       cur = nxt;
       ti = tn;
@@ -347,11 +455,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   for (int rt = 0; rt < RT; ++rt) l_run[rt] = sum_across_groups(l_run[rt]);
 
   // ---- epilogue ----------------------------------------------------------------
-  auto out_row = [&](int rr, int64_t& orow) {
+  auto out_row = [&](int rr) -> int64_t {
     const int t = rr / p.G, gg = rr % p.G;
     const int h = kvh * p.G + gg;
-    orow = ((int64_t)qb * p.sq + t) * p.Hq + h;
-    if constexpr (MODE == MODE_SEGMENT) orow = (int64_t)item * p.Hq + h;
+    if constexpr (MODE == MODE_SEGMENT) return (int64_t)item * p.Hq + h;
+    return ((int64_t)qb * p.sq + t) * p.Hq + h;
   };
   float* lse_base = p.lse;
   void* o_base = p.out;
@@ -364,22 +472,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int rr = row_base + rt * 16 + c16;
-      if (rr >= p.R) continue;
-      int64_t orow;
-      out_row(rr, orow);
-      const float l = l_run[rt];
-      const bool live = l > 0.f;
-      const float inv = live ? p.v_scale / l : 0.f;
-      if (live || !p.partial) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float vals[VPL];
-#pragma unroll
-          for (int j = 0; j < VPL; ++j) vals[j] = acc[rt][j][i] * inv;
-          store_row<VPL>(o_base, orow * D + VPL * (4 * g4 + i), p.out_kind, vals);
-        }
-      }
-      if (g4 == 0 && lse_base) lse_base[orow] = live ? (m_run[rt] + log2f(l)) * kLn2 : kNegInf;
+      if (rr < p.R)
+        store_tile<D>(acc[rt], m_run[rt], l_run[rt], p.v_scale, o_base, p.out_kind, lse_base,
+                      out_row(rr), p.partial, g4);
     }
   } else {
     __shared__ float red_o[NW][ROWS][D + 4];
@@ -404,8 +499,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
       const int dq = (e - row * QD) * 4;
       const int rr = row_base + row;
       if (rr >= p.R) continue;
-      int64_t orow;
-      out_row(rr, orow);
+      const int64_t orow = out_row(rr);
       float M = kNegInf;
 #pragma unroll
       for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w][row]);
@@ -433,40 +527,203 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   }
 }
 
-// ---- instantiation table ------------------------------------------------------
+// ================================================================================
+// attn_shared_kernel (paged): work item (request, kv head, row group, split);
+// wave w owns rows row_base + 16w .. +16, every wave attends every tile.
+//
+// LDS ring: stage s holds one tile as 16 keys x CPK 16-byte chunks, K chunks
+// first then V chunks of each key, chunk c of key t stored at position
+// t*CPK + (c ^ (t & SWZ)).  The XOR keeps the K-operand reads (16 keys, same
+// chunk) on distinct banks; direct-to-LDS loads write lane i's 16 bytes to
+// position 64*j + i of instruction j, so each lane simply fetches the chunk
+// that belongs at its position.  Instruction j of a tile is issued by wave
+// j / (IPT / NW).
+// ================================================================================
+template <int D, int NW, int KV, int QT, int NBUF>
+__global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p) {
+  using G = Geo<D, KV>;
+  constexpr int KB = G::KB;
+  constexpr int VPL = G::VPL;
+  constexpr int IPW = G::IPT / NW;  // direct-to-LDS loads per wave per tile
+  static_assert(G::IPT % NW == 0 && IPW >= 1, "tile loads must split evenly over the waves");
+  static_assert(NBUF >= 2, "ring depth");
+  __shared__ __attribute__((aligned(1024))) char ring[NBUF][G::TILE_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int g4 = lane >> 4;
+  const int c16 = lane & 15;
+
+  uint32_t bid = blockIdx.x;
+  const int split = (int)(bid % (uint32_t)p.S);
+  bid /= (uint32_t)p.S;
+  const int rg = (int)(bid % (uint32_t)p.RG);
+  bid /= (uint32_t)p.RG;
+  const int kvh = (int)(bid % (uint32_t)p.Hkv);
+  const int item = (int)(bid / (uint32_t)p.Hkv);
+
+  const int64_t ts_b = p.token_stride * KB;
+  const int64_t head_off_b = (int64_t)kvh * p.head_stride * KB;
+  const PagedRange pr = paged_range(p, item, split);
+  const int n_tiles = pr.n_tiles;
+  const int row0 = rg * (NW * 16) + wave * 16;
+
+  u32x4 qf[D / 32];
+  load_q<D, KV>(qf, p.q, row0, p.R, p.G, kvh, item, p.sq, p.Hq, g4, c16);
+
+  const int32_t* trow = p.block_table + (int64_t)item * p.bt_stride;
+  int32_t phys_vec = 0;  // lane i: pool page of tile k0 + i
+  int k0 = -64;
+
+  // Source of the chunk this lane writes for instruction j of a tile.
+  auto issue_tile = [&](int k, int stage) {
+    if (k - k0 >= 64) {
+      k0 = k;
+      const int kl = k0 + lane;
+      int32_t ph = 0;
+      if (kl < n_tiles) ph = load_phys(p, trow, pr.sv, pr.sr.first_page + kl / pr.TPP);
+      phys_vec = ph;
+    }
+    const int32_t phys = __builtin_amdgcn_readlane(phys_vec, k - k0);
+    int page, slot0, nvalid;
+    paged_tile(p, pr, k, page, slot0, nvalid);
+    const int64_t off = ((int64_t)phys * p.page_stride + (int64_t)slot0 * p.token_stride) * KB + head_off_b;
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+      const int j = wave * IPW + u;
+      const int pos = 64 * j + lane;
+      const int t = pos / G::CPK;
+      const int c = (pos % G::CPK) ^ (t & G::SWZ);
+      const int ts = t < nvalid ? t : 0;  // invalid slots fetch slot 0 (masked later)
+      const char* src = (c < G::CPK / 2) ? p.k + off + ts * ts_b + 16 * c
+                                         : p.v + off + ts * ts_b + 16 * (c - G::CPK / 2);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                       (__attribute__((address_space(3))) void*)(&ring[stage][1024 * j]),
+                                       16, 0, 2 /* nt */);
+    }
+  };
+
+  // MFMA operands of a staged tile.
+  auto read_frags = [&](int stage, Frags<D>& f) {
+    const char* st = ring[stage];
+    Raw<D, KV> r;
+    {
+      const int t = c16;
+#pragma unroll
+      for (int i = 0; i < G::KLD; ++i) {
+        const int c = 4 * i + g4;
+        r.k[i] = *reinterpret_cast<const u32x4*>(st + 16 * (t * G::CPK + (c ^ (t & G::SWZ))));
+      }
+    }
+    const int vbyte = G::VB * c16;  // byte offset of this lane's values inside a V row
+    const int cv = G::CPK / 2 + (vbyte >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * g4 + i;
+      lds_read_v<G::VDW>(r.v[i], st + 16 * (t * G::CPK + (cv ^ (t & G::SWZ))) + (vbyte & 15));
+    }
+    make_frags<D, KV, QT>(r, f);
+  };
+
+  f32x4 acc[VPL];
+  float m_run = kNegInf, l_run = 0.f;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int npro = n_tiles < NBUF - 1 ? n_tiles : NBUF - 1;
+  for (int k = 0; k < npro; ++k) issue_tile(k, k);
+
+  for (int k = 0; k < n_tiles; ++k) {
+    // tiles issued after k by this wave: min(NBUF-2, n_tiles-1-k); wait for the rest
+    const int ahead = min(NBUF - 2, n_tiles - 1 - k);
+    if constexpr (NBUF >= 4) {
+      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * IPW));
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPW));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    } else if constexpr (NBUF == 3) {
+      if (ahead >= 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPW));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    // Every wave's part of tile k has landed and every wave has consumed tile
+    // k-1 (its stage is refilled next).  A bare s_barrier: the usual
+    // workgroup fence would also wait for the tiles still in flight.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (k + NBUF - 1 < n_tiles) issue_tile(k + NBUF - 1, (k + NBUF - 1) % NBUF);
+    int page, slot0, nvalid;
+    paged_tile(p, pr, k, page, slot0, nvalid);
+    Frags<D> f;
+    read_frags(k % NBUF, f);
+    attend_tile<D, QT>(f, qf, acc, m_run, l_run, p.qk_scale_log2, 0.f, nvalid, g4);
+  }
+
+  l_run = sum_across_groups(l_run);
+  float* lse_base = p.lse;
+  void* o_base = p.out;
+  if (p.partial) {
+    lse_base = p.lse + (int64_t)split * p.split_stride_lse;
+    o_base = reinterpret_cast<float*>(p.out) + (int64_t)split * p.split_stride_o;
+  }
+  const int rr = row0 + c16;
+  if (rr < p.R) {
+    const int t = rr / p.G, gg = rr % p.G;
+    const int64_t orow = ((int64_t)item * p.sq + t) * p.Hq + kvh * p.G + gg;
+    store_tile<D>(acc, m_run, l_run, p.v_scale, o_base, p.out_kind, lse_base, orow, p.partial, g4);
+  }
+}
+
+// ---- instantiation table ------------------------------------------------------------
 namespace {
 
 using KernelFn = void (*)(AttnParams);
 
-template <int D, int RT, int NW, int KV, int QT, int MODE>
-constexpr KernelFn kfn() {
-  return attn_kernel<D, RT, NW, KV, QT, MODE>;
-}
-
 template <int D, int KV, int QT, int MODE>
-KernelFn pick_rt_nw(int RT, int NW) {
-  if (RT == 1 && NW == 4) return kfn<D, 1, 4, KV, QT, MODE>();
-  if (RT == 1 && NW == 1) return kfn<D, 1, 1, KV, QT, MODE>();
-  if (RT == 2 && NW == 2) return kfn<D, 2, 2, KV, QT, MODE>();
-  if (RT == 4 && NW == 1) return kfn<D, 4, 1, KV, QT, MODE>();
+KernelFn pick_keys(int RT, int NW) {
+  if (RT == 1 && NW == 4) return attn_kernel<D, 1, 4, KV, QT, MODE>;
+  if (RT == 1 && NW == 1) return attn_kernel<D, 1, 1, KV, QT, MODE>;
+  if (RT == 2 && NW == 2) return attn_kernel<D, 2, 2, KV, QT, MODE>;
+  if (RT == 4 && NW == 1) return attn_kernel<D, 4, 1, KV, QT, MODE>;
   return nullptr;
 }
 
+template <int D, int KV, int QT>
+KernelFn pick_rows(int NW) {
+  constexpr int IPT = Geo<D, KV>::IPT;
+  if constexpr (IPT % 8 == 0)
+    if (NW == 8) return attn_shared_kernel<D, 8, KV, QT, 4>;
+  if constexpr (IPT % 4 == 0)
+    if (NW == 4) return attn_shared_kernel<D, 4, KV, QT, 4>;
+  if (NW == 2) return attn_shared_kernel<D, 2, KV, QT, 4>;
+  return nullptr;
+}
+
+template <int D, int KV, int QT, int MODE>
+KernelFn pick_kind(const LaunchShape& s) {
+  if (s.rows_split) {
+    if constexpr (MODE == MODE_PAGED) return pick_rows<D, KV, QT>(s.NW);
+    return nullptr;
+  }
+  return pick_keys<D, KV, QT, MODE>(s.RT, s.NW);
+}
+
 template <int D, int MODE>
-KernelFn pick_types(int kv, int q, int RT, int NW) {
-  if (kv == K_BF16 && q == K_BF16) return pick_rt_nw<D, K_BF16, K_BF16, MODE>(RT, NW);
-  if (kv == K_FP16 && q == K_FP16) return pick_rt_nw<D, K_FP16, K_FP16, MODE>(RT, NW);
+KernelFn pick_types(const LaunchShape& s) {
+  if (s.kv_kind == K_BF16 && s.q_kind == K_BF16) return pick_kind<D, K_BF16, K_BF16, MODE>(s);
+  if (s.kv_kind == K_FP16 && s.q_kind == K_FP16) return pick_kind<D, K_FP16, K_FP16, MODE>(s);
   if constexpr (MODE == MODE_PAGED) {
-    if (kv == K_FP8 && q == K_BF16) return pick_rt_nw<D, K_FP8, K_BF16, MODE>(RT, NW);
-    if (kv == K_FP8 && q == K_FP16) return pick_rt_nw<D, K_FP8, K_FP16, MODE>(RT, NW);
+    if (s.kv_kind == K_FP8 && s.q_kind == K_BF16) return pick_kind<D, K_FP8, K_BF16, MODE>(s);
+    if (s.kv_kind == K_FP8 && s.q_kind == K_FP16) return pick_kind<D, K_FP8, K_FP16, MODE>(s);
   }
   return nullptr;
 }
 
 template <int MODE>
 KernelFn pick_d(const LaunchShape& s) {
-  if (s.D == 128) return pick_types<128, MODE>(s.kv_kind, s.q_kind, s.RT, s.NW);
-  if (s.D == 64) return pick_types<64, MODE>(s.kv_kind, s.q_kind, s.RT, s.NW);
+  if (s.D == 128) return pick_types<128, MODE>(s);
+  if (s.D == 64) return pick_types<64, MODE>(s);
   return nullptr;
 }
 
@@ -482,6 +739,11 @@ KernelFn pick(const LaunchShape& s) {
 }  // namespace
 
 bool attention_supported(const LaunchShape& s) { return pick(s) != nullptr; }
+
+int shared_tile_loads(int D, int kv_kind) {
+  const int kb = kv_kind == K_FP8 ? 1 : 2;
+  return 16 * 2 * D * kb / 1024;
+}
 
 hipError_t launch_attention(const AttnParams& p, const LaunchShape& s, int64_t grid,
                             hipStream_t stream) {

@@ -7,9 +7,11 @@
 // weights), output = weighted sum of the live partial outputs.  Split-KV uses
 // it with a zero prior and "live" meaning a finite partial LSE.
 //
-// One wave per (row, head): the wave reads the partial LSEs once, lanes own
-// head-dim columns d = lane, lane + 64, ... so each partial row is read with
-// one coalesced pass, and dead partial outputs are never read.
+// One wave per (row, head).  Lane s holds the logit of partial s; lanes own
+// head-dim columns d = lane + 64c.  Partial rows are fetched in batches of 8
+// independent loads per lane, issued without waiting for the logits, and a
+// dead partial's row (possibly never written) only ever meets a select, so it
+// cannot leak into the result.
 
 #include "pa_device.h"
 #include "pa_kernels.h"
@@ -20,6 +22,7 @@ namespace pa {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kBatch = 8;
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -32,10 +35,11 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float load_elem(const void* base, int64_t i, int kind) {
-  if (kind == K_F32) return reinterpret_cast<const float*>(base)[i];
+template <int PK>
+__device__ __forceinline__ float load_elem(const void* base, int64_t i) {
+  if constexpr (PK == K_F32) return reinterpret_cast<const float*>(base)[i];
   const uint16_t b = reinterpret_cast<const uint16_t*>(base)[i];
-  if (kind == K_BF16) return __uint_as_float((uint32_t)b << 16);
+  if constexpr (PK == K_BF16) return __uint_as_float((uint32_t)b << 16);
   return (float)bitcast<_Float16>(b);
 }
 
@@ -49,45 +53,65 @@ __device__ __forceinline__ void store_elem(void* base, int64_t i, int kind, floa
   }
 }
 
-// Shared merge: `logit(g)` returns the log2-domain logit of partial g or -inf
-// when dead; `elem(g, d)` reads partial g's output column d.
-template <typename LogitFn, typename ElemFn>
-__device__ __forceinline__ void merge_row(int G, int D, LogitFn logit, ElemFn elem, void* out,
-                                          int64_t out_off, int out_kind, float* lse,
-                                          int64_t lse_off) {
+// Merge G partial rows (row g at obase + g * ostride, element kind PK) of one
+// (row, head).  `logit(g)` is the natural-log logit of partial g, -inf if dead.
+// C = ceil(D / 64) head-dim columns per lane.
+template <int C, int PK, typename LogitFn>
+__device__ __forceinline__ void merge_row(int G, int D, LogitFn logit, const void* obase,
+                                          int64_t ostride, void* out, int64_t out_off,
+                                          int out_kind, float* lse, int64_t lse_off) {
   const int lane = threadIdx.x & 63;
   float M = kNegInf;
-  for (int g = lane; g < G; g += 64) M = fmaxf(M, logit(g));
+  for (int g0 = 0; g0 < G; g0 += 64) {
+    const int g = g0 + lane;
+    M = fmaxf(M, g < G ? logit(g) : kNegInf);
+  }
   M = wave_max(M);
-  if (M == kNegInf) {
-    for (int d = lane; d < D; d += 64) store_elem(out, out_off + d, out_kind, 0.f);
-    if (lse && lane == 0) lse[lse_off] = kNegInf;
-    return;
-  }
+  float o[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) o[c] = 0.f;
   float tot = 0.f;
-  for (int g = lane; g < G; g += 64) tot += fast_exp2(logit(g) - M);
-  tot = wave_sum(tot);
-  const float inv = 1.0f / tot;
-  constexpr int MAXC = 4;  // D <= 256
-  float o[MAXC] = {0.f, 0.f, 0.f, 0.f};
-  for (int g = 0; g < G; ++g) {
-    const float lg = logit(g);  // wave-uniform
-    if (lg == kNegInf) continue;
-    const float w = fast_exp2(lg - M) * inv;
+  if (M != kNegInf) {
+    for (int g0 = 0; g0 < G; g0 += 64) {
+      const int g = g0 + lane;
+      const float lg = g < G ? logit(g) : kNegInf;
+      const float w_lane = lg == kNegInf ? 0.f : fast_exp2((lg - M) * kLog2e);
+      tot += w_lane;
+      const int n = G - g0 < 64 ? G - g0 : 64;
+      for (int j = 0; j < n; j += kBatch) {
+        float x[kBatch][C];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-      const int d = lane + 64 * c;
-      if (d < D) o[c] += w * elem(g, d);
+        for (int u = 0; u < kBatch; ++u) {
+          const int gg = g0 + (j + u < n ? j + u : 0);
+#pragma unroll
+          for (int c = 0; c < C; ++c) {
+            const int d = lane + 64 * c;
+            x[u][c] = d < D ? load_elem<PK>(obase, (int64_t)gg * ostride + d) : 0.f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const float w = __shfl(w_lane, j + u < n ? j + u : 0, 64);
+          const bool use = (j + u < n) && w > 0.f;
+#pragma unroll
+          for (int c = 0; c < C; ++c) o[c] = use ? o[c] + w * x[u][c] : o[c];
+        }
+      }
     }
+    tot = wave_sum(tot);
+    const float inv = 1.f / tot;
+#pragma unroll
+    for (int c = 0; c < C; ++c) o[c] *= inv;
   }
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
+  for (int c = 0; c < C; ++c) {
     const int d = lane + 64 * c;
     if (d < D) store_elem(out, out_off + d, out_kind, o[c]);
   }
-  if (lse && lane == 0) lse[lse_off] = (M + log2f(tot)) * kLn2;
+  if (lse && lane == 0) lse[lse_off] = tot > 0.f ? M + logf(tot) : kNegInf;
 }
 
+template <int C>
 __global__ __launch_bounds__(256) void split_combine_kernel(const float* __restrict__ part_o,
                                                             const float* __restrict__ part_lse,
                                                             int32_t S, int32_t rows, int32_t Hq,
@@ -96,16 +120,13 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const float* __restr
   const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // row * Hq + head
   const int64_t total = (int64_t)rows * Hq;
   if (rh >= total) return;
-  auto logit = [&](int s) -> float {
-    const float l = part_lse[(int64_t)s * total + rh];
-    return l == kNegInf ? kNegInf : l * kLog2e;
-  };
-  auto elem = [&](int s, int d) -> float { return part_o[((int64_t)s * total + rh) * D + d]; };
-  merge_row(S, D, logit, elem, out, rh * D, out_kind, lse, rh);
+  auto logit = [&](int s) -> float { return part_lse[(int64_t)s * total + rh]; };
+  merge_row<C, K_F32>(S, D, logit, part_o + rh * D, total * D, out, rh * D, out_kind, lse, rh);
 }
 
+template <int C, int PK>
 __global__ __launch_bounds__(256) void segment_combine_kernel(
-    const void* __restrict__ part_o, int32_t part_kind, const float* __restrict__ part_lse,
+    const void* __restrict__ part_o, const float* __restrict__ part_lse,
     const int32_t* __restrict__ used, const float* __restrict__ bias, int32_t N, int32_t G,
     int32_t Hq, int32_t D, void* out, int32_t out_kind, float* lse) {
   const int64_t nh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // n * Hq + h
@@ -115,12 +136,11 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(
   auto logit = [&](int g) -> float {
     if (used[n * G + g] <= 0) return kNegInf;
     const float prior = g < G - 1 ? bias[n * (G - 1) + g] : 0.f;
-    return (part_lse[(n * G + g) * Hq + h] + prior) * kLog2e;
+    return part_lse[(n * G + g) * Hq + h] + prior;
   };
-  auto elem = [&](int g, int d) -> float {
-    return load_elem(part_o, ((n * G + g) * Hq + h) * D + d, part_kind);
-  };
-  merge_row(G, D, logit, elem, out, nh * D, out_kind, lse, nh);
+  const int64_t eb = PK == K_F32 ? 4 : 2;
+  const char* obase = static_cast<const char*>(part_o) + ((n * G) * Hq + h) * D * eb;
+  merge_row<C, PK>(G, D, logit, obase, (int64_t)Hq * D, out, nh * D, out_kind, lse, nh);
 }
 
 __global__ void describe_kernel(const int32_t* __restrict__ table, int64_t bt_stride,
@@ -146,6 +166,25 @@ __global__ void describe_kernel(const int32_t* __restrict__ table, int64_t bt_st
     }
 }
 
+template <int C>
+hipError_t launch_split_c(const float* part_o, const float* part_lse, int32_t S, int32_t rows,
+                          int32_t Hq, int32_t D, void* out, int32_t out_kind, float* lse,
+                          hipStream_t stream, int64_t grid) {
+  hipLaunchKernelGGL(split_combine_kernel<C>, dim3((unsigned)grid), dim3(256), 0, stream, part_o,
+                     part_lse, S, rows, Hq, D, out, out_kind, lse);
+  return hipGetLastError();
+}
+
+template <int C, int PK>
+hipError_t launch_segment_c(const void* part_o, const float* part_lse, const int32_t* used,
+                            const float* bias, int32_t N, int32_t G, int32_t Hq, int32_t D,
+                            void* out, int32_t out_kind, float* lse, hipStream_t stream,
+                            int64_t grid) {
+  hipLaunchKernelGGL((segment_combine_kernel<C, PK>), dim3((unsigned)grid), dim3(256), 0, stream,
+                     part_o, part_lse, used, bias, N, G, Hq, D, out, out_kind, lse);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_split_combine(const float* part_o, const float* part_lse, int32_t S,
@@ -154,9 +193,9 @@ hipError_t launch_split_combine(const float* part_o, const float* part_lse, int3
   const int64_t waves = (int64_t)rows * Hq;
   if (waves == 0) return hipSuccess;
   const int64_t grid = (waves + 3) / 4;
-  hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)grid), dim3(256), 0, stream, part_o,
-                     part_lse, S, rows, Hq, D, out, out_kind, lse);
-  return hipGetLastError();
+  if (D <= 64) return launch_split_c<1>(part_o, part_lse, S, rows, Hq, D, out, out_kind, lse, stream, grid);
+  if (D <= 128) return launch_split_c<2>(part_o, part_lse, S, rows, Hq, D, out, out_kind, lse, stream, grid);
+  return launch_split_c<4>(part_o, part_lse, S, rows, Hq, D, out, out_kind, lse, stream, grid);
 }
 
 hipError_t launch_segment_combine(const void* part_o, int32_t part_kind, const float* part_lse,
@@ -166,9 +205,19 @@ hipError_t launch_segment_combine(const void* part_o, int32_t part_kind, const f
   const int64_t waves = (int64_t)N * Hq;
   if (waves == 0) return hipSuccess;
   const int64_t grid = (waves + 3) / 4;
-  hipLaunchKernelGGL(segment_combine_kernel, dim3((unsigned)grid), dim3(256), 0, stream, part_o,
-                     part_kind, part_lse, used, bias, N, G, Hq, D, out, out_kind, lse);
-  return hipGetLastError();
+#define PA_SEG(C)                                                                                \
+  if (part_kind == K_F32)                                                                        \
+    return launch_segment_c<C, K_F32>(part_o, part_lse, used, bias, N, G, Hq, D, out, out_kind, \
+                                      lse, stream, grid);                                       \
+  if (part_kind == K_BF16)                                                                       \
+    return launch_segment_c<C, K_BF16>(part_o, part_lse, used, bias, N, G, Hq, D, out, out_kind,\
+                                       lse, stream, grid);                                      \
+  return launch_segment_c<C, K_FP16>(part_o, part_lse, used, bias, N, G, Hq, D, out, out_kind,  \
+                                     lse, stream, grid);
+  if (D <= 64) { PA_SEG(1) }
+  if (D <= 128) { PA_SEG(2) }
+  PA_SEG(4)
+#undef PA_SEG
 }
 
 hipError_t launch_describe(const int32_t* block_table, int64_t bt_stride, int32_t bt_width,

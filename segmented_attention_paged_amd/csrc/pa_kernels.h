@@ -39,9 +39,15 @@ struct AttnParams {
   int32_t topk, bs, local;
 };
 
+// rows_split = 0: attn_kernel (waves split the keys, RT row tiles per wave);
+// rows_split = 1: attn_shared_kernel (paged only; NW waves of one row tile each
+// share LDS-staged K/V tiles).
 struct LaunchShape {
-  int D, kv_kind, q_kind, RT, NW, mode;
+  int D, kv_kind, q_kind, RT, NW, mode, rows_split;
 };
+
+// 1 KiB direct-to-LDS loads per staged tile (the shared kernel needs NW to divide it).
+int shared_tile_loads(int D, int kv_kind);
 
 hipError_t launch_attention(const AttnParams& p, const LaunchShape& s, int64_t grid,
                             hipStream_t stream);

@@ -115,6 +115,27 @@ def test_zero_batch_is_noop(sap):
     sap.paged_attn_run(inp.q[:0], k, v, inp.block_table[:0], inp.seq_lens[:0], scale=0.1, out=out)
 
 
+def test_fused_combine_counters_reset_between_calls(sap):
+    """Repeated split runs sharing one workspace: the in-kernel merge counters return to
+    zero after every call, so every call produces the same (correct) result."""
+    inp = _small("block_sq16_window")
+    k, v = sap.kv_halves(inp.cache, inp.D)
+    W = inp.block_table.shape[1]
+    O, L = oracle_paged(inp)
+    for splits in (3, 5):
+        need = sap.workspace_size(inp.B, inp.sq, inp.Hq, inp.Hkv, inp.D, inp.P, W, inp.window, splits)
+        ws = sap.new_workspace(need, DEV)
+        first = None
+        for rep in range(4):
+            out, lse = sap.paged_attn_run(inp.q, k, v, inp.block_table, inp.seq_lens, scale=inp.scale,
+                                          window=inp.window, num_splits=splits, workspace=ws)
+            compare(out, lse, O, L, TOL_BF16, what=f"S={splits} rep={rep}")
+            if first is None:
+                first = (out.clone(), lse.clone())
+            else:
+                assert torch.equal(out.view(torch.int16), first[0].view(torch.int16))
+
+
 # ---- Split-KV partials and the combine ------------------------------------------
 @pytest.mark.parametrize("name,S", [("decode_d128_g4", 3), ("block_sq16_window", 5), ("page64", 2),
                                     ("fp8_bf16q", 16)])
