@@ -31,6 +31,10 @@ COMMON = [
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs: the online-softmax rescale then
+    # multiplies them in place instead of copying every accumulator out of the
+    # AGPRs and back on each tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
     "-I", CSRC,
 ]

@@ -81,9 +81,11 @@ Plan make_plan(int32_t B, int32_t sq, int32_t Hq, int32_t Hkv, int32_t D, int32_
   } else {
     // A few equal splits per request: enough workgroups to fill the chip, few
     // enough that the per-workgroup start-up and the partial round trip stay
-    // small.
+    // small.  The row-split kernel (query blocks) keeps each workgroup's waves
+    // in lock step per tile and wants twice as many workgroups.
     const int64_t items = (int64_t)B * Hkv * pl.RG;
-    int64_t S = cdiv(kTargetWorkgroups, std::max<int64_t>(items, 1));
+    const int64_t target = pl.rows_split ? 2 * kTargetWorkgroups : kTargetWorkgroups;
+    int64_t S = cdiv(target, std::max<int64_t>(items, 1));
     const int64_t min_pages_per_split = std::max<int64_t>(1, cdiv(16, cdiv(P, 16)) );
     S = std::min<int64_t>(S, std::max<int64_t>(1, pages_max / min_pages_per_split));
     S = std::max<int64_t>(1, std::min<int64_t>(S, 64));

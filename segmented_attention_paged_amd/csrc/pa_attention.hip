@@ -39,6 +39,7 @@ namespace pa {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kRescaleSlack = 8.0f;  // log2 units: softmax terms stay <= 256 before a rescale
 
 template <int D, int KV>
 struct Geo {
@@ -187,19 +188,25 @@ __device__ __forceinline__ void attend_tile(const Frags<D>& f, const u32x4 (&qf)
   }
   float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   tmax = max_across_groups(tmax);
-  const float m_new = fmaxf(m_run, tmax);
-  const float alpha = fast_exp2(m_run - m_new);
+  // Lazy rescale: the reference max m_run only moves when some row of the
+  // wave sees a logit more than kRescaleSlack above it, so p = 2^(s - m_run)
+  // stays <= 2^kRescaleSlack and the O / l rescale is skipped on most tiles.
+  // Softmax does not depend on the reference, only on it bounding the terms.
+  if (__ballot(tmax > m_run + kRescaleSlack) != 0) {
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile (m_run = -inf)
+    l_run *= alpha;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) acc[j] *= alpha;
+    m_run = m_new;
+  }
   float pr[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s[i] - m_new);
-  l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-  m_run = m_new;
+  for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s[i] - m_run);
+  l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
   const u32x2 pB = u32x2{pack2<QT>(pr[0], pr[1]), pack2<QT>(pr[2], pr[3])};
 #pragma unroll
-  for (int j = 0; j < D / 16; ++j) {
-    acc[j] *= alpha;
-    acc[j] = mfma_16x16x16<QT>(f.vA[j], pB, acc[j]);
-  }
+  for (int j = 0; j < D / 16; ++j) acc[j] = mfma_16x16x16<QT>(f.vA[j], pB, acc[j]);
 }
 
 // Write one lane's part of a finished 16-row tile: row row0 + l%16, head-dim
@@ -260,6 +267,40 @@ __device__ __forceinline__ void paged_tile(const AttnParams& p, const PagedRange
   nvalid = nv;
 }
 
+// Wait until this wave's loads of the current tile have landed, i.e. until at
+// most `ahead` later tiles (IPW loads each) are still in flight.  s_waitcnt
+// takes an immediate, hence the unrolled chain.
+template <int IPW, int A>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+  static_assert(A * IPW <= 63, "vmcnt holds at most 63 outstanding loads");
+  if constexpr (A <= 0) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  } else {
+    if (ahead >= A) __builtin_amdgcn_s_waitcnt(vmcnt_imm(A * IPW));
+    else wait_tiles_ahead<IPW, A - 1>(ahead);
+  }
+}
+
+// Longest-first dispatch: the request with the given rank when requests are
+// ordered by decreasing visible length (ties by index).  Work items are laid
+// out rank-major, so the hardware starts the longest requests' workgroups
+// first and the short ones fill the tail.  Every wave of the workgroup
+// computes it (one 64-wide load and a 64-step compare).  Used for up to 64
+// requests; larger batches keep their natural order.
+__device__ __forceinline__ int request_of_rank(const AttnParams& p, int rank) {
+  if (p.items > 64) return rank;
+  const int lane = threadIdx.x & 63;
+  int len = -1;
+  if (lane < p.items) len = seq_view(p.seq_lens[lane], p.window, p.sq, p.P, p.bt_width).len;
+  int r = 0;
+  for (int j = 0; j < p.items; ++j) {
+    const int lj = __builtin_amdgcn_readlane(len, j);
+    r += (lj > len) | ((lj == len) & (j < lane));
+  }
+  const uint64_t hit = __ballot(lane < p.items && r == rank);
+  return (int)__builtin_ctzll(hit);
+}
+
 // Pool page of restricted page `page`, clamped into the pool.
 __device__ __forceinline__ int32_t load_phys(const AttnParams& p, const int32_t* trow,
                                              const SeqView& sv, int page) {
@@ -296,7 +337,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   const int rg = (int)(bid % (uint32_t)p.RG);
   bid /= (uint32_t)p.RG;
   const int kvh = (int)(bid % (uint32_t)p.Hkv);
-  const int item = (int)(bid / (uint32_t)p.Hkv);
+  int item = (int)(bid / (uint32_t)p.Hkv);
+  if constexpr (MODE == MODE_PAGED) item = request_of_rank(p, item);
 
   const int64_t ts_b = p.token_stride * KB;
   const int64_t head_off_b = (int64_t)kvh * p.head_stride * KB;
@@ -560,7 +602,7 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
   const int rg = (int)(bid % (uint32_t)p.RG);
   bid /= (uint32_t)p.RG;
   const int kvh = (int)(bid % (uint32_t)p.Hkv);
-  const int item = (int)(bid / (uint32_t)p.Hkv);
+  const int item = request_of_rank(p, (int)(bid / (uint32_t)p.Hkv));
 
   const int64_t ts_b = p.token_stride * KB;
   const int64_t head_off_b = (int64_t)kvh * p.head_stride * KB;
@@ -635,17 +677,7 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
 
   for (int k = 0; k < n_tiles; ++k) {
     // tiles issued after k by this wave: min(NBUF-2, n_tiles-1-k); wait for the rest
-    const int ahead = min(NBUF - 2, n_tiles - 1 - k);
-    if constexpr (NBUF >= 4) {
-      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * IPW));
-      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPW));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    } else if constexpr (NBUF == 3) {
-      if (ahead >= 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPW));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
+    wait_tiles_ahead<IPW, NBUF - 2>(min(NBUF - 2, n_tiles - 1 - k));
     // Every wave's part of tile k has landed and every wave has consumed tile
     // k-1 (its stage is refilled next).  A bare s_barrier: the usual
     // workgroup fence would also wait for the tiles still in flight.
@@ -678,6 +710,11 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
 // ---- instantiation table ------------------------------------------------------------
 namespace {
 
+#ifndef PA_RING_STAGES
+#define PA_RING_STAGES 4
+#endif
+constexpr int kRingStages = PA_RING_STAGES;  // LDS ring depth of attn_shared_kernel
+
 using KernelFn = void (*)(AttnParams);
 
 template <int D, int KV, int QT, int MODE>
@@ -693,10 +730,10 @@ template <int D, int KV, int QT>
 KernelFn pick_rows(int NW) {
   constexpr int IPT = Geo<D, KV>::IPT;
   if constexpr (IPT % 8 == 0)
-    if (NW == 8) return attn_shared_kernel<D, 8, KV, QT, 4>;
+    if (NW == 8) return attn_shared_kernel<D, 8, KV, QT, kRingStages>;
   if constexpr (IPT % 4 == 0)
-    if (NW == 4) return attn_shared_kernel<D, 4, KV, QT, 4>;
-  if (NW == 2) return attn_shared_kernel<D, 2, KV, QT, 4>;
+    if (NW == 4) return attn_shared_kernel<D, 4, KV, QT, kRingStages>;
+  if (NW == 2) return attn_shared_kernel<D, 2, KV, QT, kRingStages>;
   return nullptr;
 }
 
