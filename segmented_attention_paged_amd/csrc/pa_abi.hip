@@ -86,7 +86,10 @@ Plan make_plan(int32_t B, int32_t sq, int32_t Hq, int32_t Hkv, int32_t D, int32_
     const int64_t items = (int64_t)B * Hkv * pl.RG;
     const int64_t target = pl.rows_split ? 2 * kTargetWorkgroups : kTargetWorkgroups;
     int64_t S = cdiv(target, std::max<int64_t>(items, 1));
-    const int64_t min_pages_per_split = std::max<int64_t>(1, cdiv(16, cdiv(P, 16)) );
+    // at least 16 tiles per split (32 for the row-split kernel, whose waves
+    // all walk every tile) so start-up and the partial write stay amortized
+    const int64_t min_tiles = pl.rows_split ? 32 : 16;
+    const int64_t min_pages_per_split = std::max<int64_t>(1, cdiv(min_tiles, cdiv(P, 16)));
     S = std::min<int64_t>(S, std::max<int64_t>(1, pages_max / min_pages_per_split));
     S = std::max<int64_t>(1, std::min<int64_t>(S, 64));
     pl.S = (int)S;

@@ -257,7 +257,8 @@ __device__ __forceinline__ PagedRange paged_range(const AttnParams& p, int item,
 // Tile `it` of a paged split: page, first slot and number of visible slots.
 __device__ __forceinline__ void paged_tile(const AttnParams& p, const PagedRange& r, int it,
                                            int& page, int& slot0, int& nvalid) {
-  const int pin = it / r.TPP, u = it - pin * r.TPP;
+  const int pin = r.TPP == 1 ? it : it / r.TPP;  // pages of up to 16 slots: no division
+  const int u = it - pin * r.TPP;
   page = r.sr.first_page + pin;
   slot0 = 16 * u;
   const int tok0 = page * p.P + slot0;
@@ -410,7 +411,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
         k0 = k;
         const int itl = wave + NW * (k0 + lane);
         int32_t ph = 0;
-        if (itl < n_tiles) ph = load_phys(p, trow, pr.sv, pr.sr.first_page + itl / pr.TPP);
+        if (itl < n_tiles)
+          ph = load_phys(p, trow, pr.sv, pr.sr.first_page + (pr.TPP == 1 ? itl : itl / pr.TPP));
         phys_vec = ph;
       }
       const int32_t phys = __builtin_amdgcn_readlane(phys_vec, k - k0);
@@ -617,53 +619,91 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
   int32_t phys_vec = 0;  // lane i: pool page of tile k0 + i
   int k0 = -64;
 
-  // Source of the chunk this lane writes for instruction j of a tile.
-  auto issue_tile = [&](int k, int stage) {
+  // Lane-constant part of the source address of each chunk this wave copies:
+  // instruction j = wave*IPW + u writes LDS position 64*j + lane, which holds
+  // chunk c of key t (see the layout above).  Relative to K of slot 0 of a
+  // tile; V chunks add the V - K distance.  `src0` is the same chunk of slot 0,
+  // fetched instead when key t is past the end of a partial tile.
+  const int64_t vk = p.v - p.k;
+  int64_t src_full[IPW], src_slot0[IPW];
+  int src_key[IPW];
+#pragma unroll
+  for (int u = 0; u < IPW; ++u) {
+    const int pos = 64 * (wave * IPW + u) + lane;
+    const int t = pos / G::CPK;
+    const int c = (pos % G::CPK) ^ (t & G::SWZ);
+    const int64_t cb = c < G::CPK / 2 ? 16 * c : vk + 16 * (c - G::CPK / 2);
+    src_slot0[u] = cb;
+    src_full[u] = cb + t * ts_b;
+    src_key[u] = t;
+  }
+  const int64_t page_b = p.page_stride * KB;
+  const int TPP = pr.TPP;
+
+  // Tile cursor: restricted page, sub-tile, first key (tiles are visited in order).
+  struct Cursor {
+    int page, u, tok0;
+  };
+  auto cursor_at0 = [&]() { return Cursor{pr.sr.first_page, 0, pr.sr.first_page * p.P}; };
+  auto advance = [&](Cursor& c) {
+    if (++c.u == TPP) {
+      c.u = 0;
+      ++c.page;
+      c.tok0 = c.page * p.P;
+    } else {
+      c.tok0 += 16;
+    }
+  };
+  auto cursor_valid = [&](const Cursor& c) {
+    int nv = p.P - 16 * c.u;
+    if (nv > 16) nv = 16;
+    if (pr.tok_end - c.tok0 < nv) nv = pr.tok_end - c.tok0;
+    return nv;
+  };
+
+  auto issue_tile = [&](int k, const Cursor& c, int stage) {
     if (k - k0 >= 64) {
       k0 = k;
       const int kl = k0 + lane;
       int32_t ph = 0;
-      if (kl < n_tiles) ph = load_phys(p, trow, pr.sv, pr.sr.first_page + kl / pr.TPP);
+      if (kl < n_tiles) ph = load_phys(p, trow, pr.sv, pr.sr.first_page + (TPP == 1 ? kl : kl / TPP));
       phys_vec = ph;
     }
     const int32_t phys = __builtin_amdgcn_readlane(phys_vec, k - k0);
-    int page, slot0, nvalid;
-    paged_tile(p, pr, k, page, slot0, nvalid);
-    const int64_t off = ((int64_t)phys * p.page_stride + (int64_t)slot0 * p.token_stride) * KB + head_off_b;
+    const char* tile = p.k + ((int64_t)phys * page_b + (int64_t)(16 * c.u) * ts_b + head_off_b);
+    const int nvalid = cursor_valid(c);
 #pragma unroll
     for (int u = 0; u < IPW; ++u) {
-      const int j = wave * IPW + u;
-      const int pos = 64 * j + lane;
-      const int t = pos / G::CPK;
-      const int c = (pos % G::CPK) ^ (t & G::SWZ);
-      const int ts = t < nvalid ? t : 0;  // invalid slots fetch slot 0 (masked later)
-      const char* src = (c < G::CPK / 2) ? p.k + off + ts * ts_b + 16 * c
-                                         : p.v + off + ts * ts_b + 16 * (c - G::CPK / 2);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                       (__attribute__((address_space(3))) void*)(&ring[stage][1024 * j]),
+      const int64_t off = (nvalid == 16 || src_key[u] < nvalid) ? src_full[u] : src_slot0[u];
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(tile + off),
+                                       (__attribute__((address_space(3))) void*)(&ring[stage][1024 * (wave * IPW + u)]),
                                        16, 0, 2 /* nt */);
     }
   };
 
-  // MFMA operands of a staged tile.
-  auto read_frags = [&](int stage, Frags<D>& f) {
-    const char* st = ring[stage];
-    Raw<D, KV> r;
-    {
-      const int t = c16;
+  // MFMA operands of a staged tile (LDS addresses are lane constants).
+  int k_lds[G::KLD], v_lds[4];
 #pragma unroll
-      for (int i = 0; i < G::KLD; ++i) {
-        const int c = 4 * i + g4;
-        r.k[i] = *reinterpret_cast<const u32x4*>(st + 16 * (t * G::CPK + (c ^ (t & G::SWZ))));
-      }
-    }
+  for (int i = 0; i < G::KLD; ++i) {
+    const int t = c16, c = 4 * i + g4;
+    k_lds[i] = 16 * (t * G::CPK + (c ^ (t & G::SWZ)));
+  }
+  {
     const int vbyte = G::VB * c16;  // byte offset of this lane's values inside a V row
     const int cv = G::CPK / 2 + (vbyte >> 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 4 * g4 + i;
-      lds_read_v<G::VDW>(r.v[i], st + 16 * (t * G::CPK + (cv ^ (t & G::SWZ))) + (vbyte & 15));
+      v_lds[i] = 16 * (t * G::CPK + (cv ^ (t & G::SWZ))) + (vbyte & 15);
     }
+  }
+  auto read_frags = [&](int stage, Frags<D>& f) {
+    const char* st = ring[stage];
+    Raw<D, KV> r;
+#pragma unroll
+    for (int i = 0; i < G::KLD; ++i) r.k[i] = *reinterpret_cast<const u32x4*>(st + k_lds[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_read_v<G::VDW>(r.v[i], st + v_lds[i]);
     make_frags<D, KV, QT>(r, f);
   };
 
@@ -672,8 +712,13 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
 #pragma unroll
   for (int j = 0; j < VPL; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  Cursor ci = cursor_at0();  // next tile to issue
+  Cursor cc = cursor_at0();  // next tile to consume
   const int npro = n_tiles < NBUF - 1 ? n_tiles : NBUF - 1;
-  for (int k = 0; k < npro; ++k) issue_tile(k, k);
+  for (int k = 0; k < npro; ++k) {
+    issue_tile(k, ci, k);
+    advance(ci);
+  }
 
   for (int k = 0; k < n_tiles; ++k) {
     // tiles issued after k by this wave: min(NBUF-2, n_tiles-1-k); wait for the rest
@@ -684,9 +729,12 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (k + NBUF - 1 < n_tiles) issue_tile(k + NBUF - 1, (k + NBUF - 1) % NBUF);
-    int page, slot0, nvalid;
-    paged_tile(p, pr, k, page, slot0, nvalid);
+    if (k + NBUF - 1 < n_tiles) {
+      issue_tile(k + NBUF - 1, ci, (k + NBUF - 1) % NBUF);
+      advance(ci);
+    }
+    const int nvalid = cursor_valid(cc);
+    advance(cc);
     Frags<D> f;
     read_frags(k % NBUF, f);
     attend_tile<D, QT>(f, qf, acc, m_run, l_run, p.qk_scale_log2, 0.f, nvalid, g4);
