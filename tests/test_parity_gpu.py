@@ -49,6 +49,10 @@ SMALL = {
                       kv_dtype="fp8_e4m3"),
     "fp8_sq16_window": dict(B=2, sq=16, Hq=8, Hkv=2, D=64, P=16, seq_lens=[20, 400],
                             kv_dtype="fp8_e4m3", window=64),
+    "decode_sq4_window": dict(B=3, sq=4, Hq=8, Hkv=2, D=128, P=16, seq_lens=[4, 60, 300],
+                              window=40),
+    "page1": dict(B=2, sq=1, Hq=4, Hkv=2, D=64, P=1, seq_lens=[5, 40]),
+    "many_requests": dict(B=70, sq=1, Hq=8, Hkv=2, D=64, P=16, seq_lens=("uniform", 0, 200)),
 }
 SPLITS = [1, 0, 3, -2]
 
@@ -134,6 +138,73 @@ def test_fused_combine_counters_reset_between_calls(sap):
                 first = (out.clone(), lse.clone())
             else:
                 assert torch.equal(out.view(torch.int16), first[0].view(torch.int16))
+
+
+@pytest.mark.parametrize("name,splits", [("decode_d128_g4", 3), ("block_sq16_window", 2),
+                                         ("decode_d64_g8", 1)])
+def test_graph_capture_replays(sap, name, splits):
+    """paged_attn_run captured into a graph (attention + combine) and replayed with eager
+    work in between: every replay equals the eager result."""
+    inp = _small(name)
+    k, v = sap.kv_halves(inp.cache, inp.D)
+    W = inp.block_table.shape[1]
+    ws = sap.new_workspace(sap.workspace_size(inp.B, inp.sq, inp.Hq, inp.Hkv, inp.D, inp.P, W,
+                                              inp.window, splits), DEV)
+    out = torch.empty((inp.B, inp.sq, inp.Hq, inp.D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((inp.B, inp.sq, inp.Hq), dtype=torch.float32, device=DEV)
+
+    def call():
+        sap.paged_attn_run(inp.q, k, v, inp.block_table, inp.seq_lens, scale=inp.scale,
+                           window=inp.window, num_splits=splits, out=out, lse=lse, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    O, L = oracle_paged(inp)
+    compare(ref_o, ref_l, O, L, TOL_BF16, what=f"{name} eager")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(lse, ref_l), f"replay {rep}"
+
+
+def test_graph_capture_segments(sap):
+    s = make_segments(seed=17, poison=True, zero_frac=0.25, name="graph", **SEG["seg_small"]).to(DEV)
+    out = torch.empty((s.N, s.Hq, s.D), dtype=torch.bfloat16, device=DEV)
+    ws = sap.new_workspace(sap.segment_attn_workspace_size(s.N, s.topk, s.Hq, s.D), DEV)
+    for fused in (True, False):
+        def call():
+            sap.segment_attn_run(s.q, s.k, s.v, s.used, s.bias, bs=s.bs, local=s.local, fused=fused,
+                                 out=out, workspace=ws, return_lse=False)
+        call()
+        torch.cuda.synchronize()
+        ref = out.clone()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            call()
+        torch.cuda.current_stream().wait_stream(st)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call()
+        for rep in range(3):
+            out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"fused={fused} {rep}"
 
 
 # ---- Split-KV partials and the combine ------------------------------------------
