@@ -13,6 +13,14 @@
 #include "pa_kernels.h"
 #include "pa_plan.h"
 
+// waves per workgroup of the segment kernels (one 16-row query group per wave set)
+#ifndef PA_SEG_FUSED_WAVES
+#define PA_SEG_FUSED_WAVES 4
+#endif
+#ifndef PA_SEG_WAVES
+#define PA_SEG_WAVES 1
+#endif
+
 using namespace pa;
 
 namespace {
@@ -81,14 +89,13 @@ Plan make_plan(int32_t B, int32_t sq, int32_t Hq, int32_t Hkv, int32_t D, int32_
   } else {
     // A few equal splits per request: enough workgroups to fill the chip, few
     // enough that the per-workgroup start-up and the partial round trip stay
-    // small.  The row-split kernel (query blocks) keeps each workgroup's waves
-    // in lock step per tile and wants twice as many workgroups.
+    // small.  The partials of the row-split kernel (query blocks) are R rows
+    // per item, so it takes fewer, longer splits.
     const int64_t items = (int64_t)B * Hkv * pl.RG;
-    const int64_t target = pl.rows_split ? 2 * kTargetWorkgroups : kTargetWorkgroups;
-    int64_t S = cdiv(target, std::max<int64_t>(items, 1));
-    // at least 16 tiles per split (32 for the row-split kernel, whose waves
-    // all walk every tile) so start-up and the partial write stay amortized
-    const int64_t min_tiles = pl.rows_split ? 32 : 16;
+    int64_t S = cdiv(kTargetWorkgroups, std::max<int64_t>(items, 1));
+    // at least 16 tiles per split (64 for the row-split kernel) so start-up
+    // and the partial write stay amortized
+    const int64_t min_tiles = pl.rows_split ? 64 : 16;
     const int64_t min_pages_per_split = std::max<int64_t>(1, cdiv(min_tiles, cdiv(P, 16)));
     S = std::min<int64_t>(S, std::max<int64_t>(1, pages_max / min_pages_per_split));
     S = std::max<int64_t>(1, std::min<int64_t>(S, 64));
@@ -380,7 +387,7 @@ int segment_attn_run(const void* q, int32_t q_dtype, const void* k, const void* 
   p.bs = bs;
   p.local = local;
   if (fused) {
-    const int NW = 4 / RT;
+    const int NW = RT == 1 ? PA_SEG_FUSED_WAVES : 4 / RT;
     p.items = N;
     p.out = out;
     p.out_kind = out_dtype;
@@ -398,7 +405,7 @@ int segment_attn_run(const void* q, int32_t q_dtype, const void* k, const void* 
   const int64_t rows = (int64_t)N * Gs * Hq;
   float* part_o = static_cast<float*>(workspace);
   float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * D * 4));
-  const int NW = RT == 1 ? 1 : 4 / RT;
+  const int NW = RT == 1 ? PA_SEG_WAVES : 4 / RT;
   p.items = N * Gs;
   p.out = part_o;
   p.out_kind = PA_F32;

@@ -30,6 +30,8 @@
 //                       VGPR staging, NBUF-1 tiles in flight.  Used for query
 //                       blocks with more than 16 rows.
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_kernels.h"
 #include "pa_plan.h"
@@ -209,10 +211,12 @@ __device__ __forceinline__ void attend_tile(const Frags<D>& f, const u32x4 (&qf)
   for (int j = 0; j < D / 16; ++j) acc[j] = mfma_16x16x16<QT>(f.vA[j], pB, acc[j]);
 }
 
-// Write one lane's part of a finished 16-row tile: row row0 + l%16, head-dim
-// values VPL*(4*(l/16)+i) + j = acc[j][i] / l (times v_scale).  Partial
-// outputs (fp32) of rows that saw no key are skipped; their LSE is -inf.
-template <int D>
+// Write one lane's part of a finished 16-row tile: row row0 + l%16, values
+// acc[j][i] / l (times v_scale) at head dim
+//   interleaved layout (BLOCKED = false):  VPL*(4*(l/16)+i) + j
+//   blocked layout     (BLOCKED = true):   16*j + 4*(l/16) + i
+// Partial outputs (fp32) of rows that saw no key are skipped; their LSE is -inf.
+template <int D, bool BLOCKED = false>
 __device__ __forceinline__ void store_tile(const f32x4 (&acc)[D / 16], float m_run, float l_run,
                                            float v_scale, void* out, int out_kind, float* lse,
                                            int64_t orow, bool partial, int g4) {
@@ -220,12 +224,20 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[D / 16], float m_r
   const bool live = l_run > 0.f;
   const float inv = live ? v_scale / l_run : 0.f;
   if (live || !partial) {
+    if constexpr (BLOCKED) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float vals[VPL];
+      for (int j = 0; j < VPL; ++j) {
+        const float vals[4] = {acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv};
+        store_row<4>(out, orow * D + 16 * j + 4 * g4, out_kind, vals);
+      }
+    } else {
 #pragma unroll
-      for (int j = 0; j < VPL; ++j) vals[j] = acc[j][i] * inv;
-      store_row<VPL>(out, orow * D + VPL * (4 * g4 + i), out_kind, vals);
+      for (int i = 0; i < 4; ++i) {
+        float vals[VPL];
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) vals[j] = acc[j][i] * inv;
+        store_row<VPL>(out, orow * D + VPL * (4 * g4 + i), out_kind, vals);
+      }
     }
   }
   if (g4 == 0 && lse) lse[orow] = live ? (m_run + log2f(l_run)) * kLn2 : kNegInf;
@@ -521,24 +533,32 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
                       out_row(rr), p.partial, g4);
     }
   } else {
-    __shared__ float red_o[NW][ROWS][D + 4];
-    __shared__ float red_m[NW][ROWS];
-    __shared__ float red_l[NW][ROWS];
+    // merge buffer in dynamic LDS, sized by the rows that exist: rows of this
+    // workgroup at or past p.R are never written or read
+    extern __shared__ float merge_lds[];
+    const int rows_held = merge_rows(p.R, ROWS);
+    constexpr int OS = D + 4;  // padded row stride
+    float* red_o = merge_lds;                          // [NW][rows_held][OS]
+    float* red_m = merge_lds + NW * rows_held * OS;    // [NW][rows_held]
+    float* red_l = red_m + NW * rows_held;             // [NW][rows_held]
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int row = rt * 16 + c16;
+      if (row < rows_held) {
+        float* dst = red_o + (wave * rows_held + row) * OS;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < VPL; ++j) red_o[wave][row][VPL * (4 * g4 + i) + j] = acc[rt][j][i];
-      if (g4 == 0) {
-        red_m[wave][row] = m_run[rt];
-        red_l[wave][row] = l_run[rt];
+          for (int j = 0; j < VPL; ++j) dst[VPL * (4 * g4 + i) + j] = acc[rt][j][i];
+        if (g4 == 0) {
+          red_m[wave * rows_held + row] = m_run[rt];
+          red_l[wave * rows_held + row] = l_run[rt];
+        }
       }
     }
     __syncthreads();
     constexpr int QD = D / 4;
-    for (int e = threadIdx.x; e < ROWS * QD; e += NW * 64) {
+    for (int e = threadIdx.x; e < rows_held * QD; e += NW * 64) {
       const int row = e / QD;
       const int dq = (e - row * QD) * 4;
       const int rr = row_base + row;
@@ -546,22 +566,23 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
       const int64_t orow = out_row(rr);
       float M = kNegInf;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w][row]);
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w * rows_held + row]);
       float o[4] = {0.f, 0.f, 0.f, 0.f};
       float tot = 0.f;
       if (M != kNegInf) {
         float wgt[NW];
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-          wgt[w] = fast_exp2(red_m[w][row] - M);
-          tot += wgt[w] * red_l[w][row];
+          wgt[w] = fast_exp2(red_m[w * rows_held + row] - M);
+          tot += wgt[w] * red_l[w * rows_held + row];
         }
         const float inv = p.v_scale / tot;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
           const float c = wgt[w] * inv;
+          const float* src = red_o + (w * rows_held + row) * OS + dq;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) o[q] += c * red_o[w][row][dq + q];
+          for (int q = 0; q < 4; ++q) o[q] += c * src[q];
         }
       }
       const bool live = tot > 0.f;
@@ -590,8 +611,22 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
   constexpr int VPL = G::VPL;
   constexpr int IPW = G::IPT / NW;  // direct-to-LDS loads per wave per tile
   static_assert(G::IPT % NW == 0 && IPW >= 1, "tile loads must split evenly over the waves");
-  static_assert(NBUF >= 2, "ring depth");
-  __shared__ __attribute__((aligned(1024))) char ring[NBUF][G::TILE_BYTES];
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
+  // One LDS object per ring stage, addressed with compile-time stage numbers
+  // (the tile loop is unrolled NBUF times).  The compiler can then tell that
+  // reading stage s does not depend on the direct-to-LDS loads still landing
+  // in the other stages; with a single array it waits for all of them first.
+  __shared__ __attribute__((aligned(1024))) char ring0[G::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char ring1[G::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char ring2[NBUF > 2 ? G::TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char ring3[NBUF > 3 ? G::TILE_BYTES : 16];
+  auto stage_buf = [&](auto sc) -> char* {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s == 0) return ring0;
+    else if constexpr (s == 1) return ring1;
+    else if constexpr (s == 2) return ring2;
+    else return ring3;
+  };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -615,9 +650,16 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
   u32x4 qf[D / 32];
   load_q<D, KV>(qf, p.q, row0, p.R, p.G, kvh, item, p.sq, p.Hq, g4, c16);
 
+  // Pool pages, 64 tiles at a time: lane i of phys_vec holds the page of tile
+  // k0 + i.  Lanes past the last tile read a valid (clamped) column that is
+  // never used; entries are clamped into the pool where they are used.
   const int32_t* trow = p.block_table + (int64_t)item * p.bt_stride;
-  int32_t phys_vec = 0;  // lane i: pool page of tile k0 + i
-  int k0 = -64;
+  auto table_batch = [&](int first) -> int32_t {
+    const int kl = first + lane;
+    return trow[table_column(pr.sv, pr.sr.first_page + (pr.TPP == 1 ? kl : kl / pr.TPP), p.bt_width)];
+  };
+  int32_t phys_vec = table_batch(0);
+  int k0 = 0;
 
   // Lane-constant part of the source address of each chunk this wave copies:
   // instruction j = wave*IPW + u writes LDS position 64*j + lane, which holds
@@ -625,16 +667,15 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
   // tile; V chunks add the V - K distance.  `src0` is the same chunk of slot 0,
   // fetched instead when key t is past the end of a partial tile.
   const int64_t vk = p.v - p.k;
-  int64_t src_full[IPW], src_slot0[IPW];
+  int64_t src_slot0[IPW], src_key_off[IPW];
   int src_key[IPW];
 #pragma unroll
   for (int u = 0; u < IPW; ++u) {
     const int pos = 64 * (wave * IPW + u) + lane;
     const int t = pos / G::CPK;
     const int c = (pos % G::CPK) ^ (t & G::SWZ);
-    const int64_t cb = c < G::CPK / 2 ? 16 * c : vk + 16 * (c - G::CPK / 2);
-    src_slot0[u] = cb;
-    src_full[u] = cb + t * ts_b;
+    src_slot0[u] = c < G::CPK / 2 ? 16 * c : vk + 16 * (c - G::CPK / 2);
+    src_key_off[u] = t * ts_b;
     src_key[u] = t;
   }
   const int64_t page_b = p.page_stride * KB;
@@ -661,34 +702,51 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
     return nv;
   };
 
-  auto issue_tile = [&](int k, const Cursor& c, int stage) {
-    if (k - k0 >= 64) {
+  auto issue_tile = [&](int k, const Cursor& c, auto sc) {
+    if (k - k0 >= 64) {  // next batch: waits for its table load (once per 64 tiles)
       k0 = k;
-      const int kl = k0 + lane;
-      int32_t ph = 0;
-      if (kl < n_tiles) ph = load_phys(p, trow, pr.sv, pr.sr.first_page + (TPP == 1 ? kl : kl / TPP));
-      phys_vec = ph;
+      phys_vec = table_batch(k0);
     }
-    const int32_t phys = __builtin_amdgcn_readlane(phys_vec, k - k0);
+    int32_t phys = __builtin_amdgcn_readlane(phys_vec, k - k0);
+    phys = phys < 0 ? 0 : (phys >= p.num_pages ? p.num_pages - 1 : phys);
+    char* ring = stage_buf(sc);
     const char* tile = p.k + ((int64_t)phys * page_b + (int64_t)(16 * c.u) * ts_b + head_off_b);
     const int nvalid = cursor_valid(c);
 #pragma unroll
     for (int u = 0; u < IPW; ++u) {
-      const int64_t off = (nvalid == 16 || src_key[u] < nvalid) ? src_full[u] : src_slot0[u];
+      const int64_t off = src_slot0[u] + ((nvalid == 16 || src_key[u] < nvalid) ? src_key_off[u] : 0);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(tile + off),
-                                       (__attribute__((address_space(3))) void*)(&ring[stage][1024 * (wave * IPW + u)]),
+                                       (__attribute__((address_space(3))) void*)(ring + 1024 * (wave * IPW + u)),
                                        16, 0, 2 /* nt */);
     }
   };
 
   // MFMA operands of a staged tile (LDS addresses are lane constants).
-  int k_lds[G::KLD], v_lds[4];
+  //  16-bit K/V: V^T comes straight from transposing LDS reads
+  //  (ds_read_b64_tr_b16), PV MFMA j covering head dims 16j .. 16j+15 (the
+  //  blocked output layout).  Within each 16-lane group, lane r of such a read
+  //  receives element r%4 of the 8-byte pieces addressed by lanes
+  //  r/4 + 4e, e = 0..3 of its group.  So the lane with a = l%4,
+  //  e = (l%16)/4 addresses dims 16j + 4a .. +3 of key 4*(l/16) + e, and lane
+  //  l receives dim 16j + l%16 of keys 4*(l/16) + e: the A operand of V^T.
+  //  fp8 K/V: V rows are read as stored and transposed in registers (the
+  //  interleaved layout), after the fp8 -> 16-bit conversion.
+  constexpr bool TR = KV != K_FP8;
+  constexpr int NVL = TR ? VPL : 4;
+  int k_lds[G::KLD], v_lds[NVL];
 #pragma unroll
   for (int i = 0; i < G::KLD; ++i) {
     const int t = c16, c = 4 * i + g4;
     k_lds[i] = 16 * (t * G::CPK + (c ^ (t & G::SWZ)));
   }
-  {
+  if constexpr (TR) {
+    const int t = 4 * g4 + (c16 >> 2), a = c16 & 3;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int cv = G::CPK / 2 + 2 * j + (a >> 1);  // 32 bytes of V per j, 8 per a
+      v_lds[j] = 16 * (t * G::CPK + (cv ^ (t & G::SWZ))) + 8 * (a & 1);
+    }
+  } else {
     const int vbyte = G::VB * c16;  // byte offset of this lane's values inside a V row
     const int cv = G::CPK / 2 + (vbyte >> 4);
 #pragma unroll
@@ -697,14 +755,23 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
       v_lds[i] = 16 * (t * G::CPK + (cv ^ (t & G::SWZ))) + (vbyte & 15);
     }
   }
-  auto read_frags = [&](int stage, Frags<D>& f) {
-    const char* st = ring[stage];
-    Raw<D, KV> r;
+  auto read_frags = [&](auto sc, Frags<D>& f) {
+    const char* st = stage_buf(sc);
+    if constexpr (TR) {
 #pragma unroll
-    for (int i = 0; i < G::KLD; ++i) r.k[i] = *reinterpret_cast<const u32x4*>(st + k_lds[i]);
+      for (int kc = 0; kc < G::NKC; ++kc) f.kf[kc] = *reinterpret_cast<const u32x4*>(st + k_lds[kc]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_read_v<G::VDW>(r.v[i], st + v_lds[i]);
-    make_frags<D, KV, QT>(r, f);
+      for (int j = 0; j < VPL; ++j)
+        f.vA[j] = bitcast<u32x2>(__builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(st + v_lds[j])));
+    } else {
+      Raw<D, KV> r;
+#pragma unroll
+      for (int i = 0; i < G::KLD; ++i) r.k[i] = *reinterpret_cast<const u32x4*>(st + k_lds[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds_read_v<G::VDW>(r.v[i], st + v_lds[i]);
+      make_frags<D, KV, QT>(r, f);
+    }
   };
 
   f32x4 acc[VPL];
@@ -714,13 +781,31 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
 
   Cursor ci = cursor_at0();  // next tile to issue
   Cursor cc = cursor_at0();  // next tile to consume
-  const int npro = n_tiles < NBUF - 1 ? n_tiles : NBUF - 1;
-  for (int k = 0; k < npro; ++k) {
-    issue_tile(k, ci, k);
-    advance(ci);
-  }
+  // prologue: tiles 0 .. NBUF-2 into stages 0 .. NBUF-2
+  auto prologue = [&](auto sc) {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s < NBUF - 1) {
+      if (s < n_tiles) {
+        issue_tile(s, ci, sc);
+        advance(ci);
+      }
+    }
+  };
+  prologue(std::integral_constant<int, 0>{});
+  prologue(std::integral_constant<int, 1>{});
+  prologue(std::integral_constant<int, 2>{});
+  // Settle the query fragments (and the first table batch) here, behind the
+  // prologue's loads.  Left to the first use inside the tile loop, the wait
+  // would stay in the loop and, merged with the ring loads of the previous
+  // iteration, drain every load in flight on each tile.
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) asm volatile("" ::"v"(qf[i]));
+  asm volatile("" ::"v"(phys_vec));
 
-  for (int k = 0; k < n_tiles; ++k) {
+  // Tile k sits in stage k % NBUF; returns false once every tile is done.
+  auto step = [&](auto sc, int k) -> bool {
+    constexpr int s = decltype(sc)::value;
+    if (k >= n_tiles) return false;
     // tiles issued after k by this wave: min(NBUF-2, n_tiles-1-k); wait for the rest
     wait_tiles_ahead<IPW, NBUF - 2>(min(NBUF - 2, n_tiles - 1 - k));
     // Every wave's part of tile k has landed and every wave has consumed tile
@@ -730,14 +815,23 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (k + NBUF - 1 < n_tiles) {
-      issue_tile(k + NBUF - 1, ci, (k + NBUF - 1) % NBUF);
+      issue_tile(k + NBUF - 1, ci, std::integral_constant<int, (s + NBUF - 1) % NBUF>{});
       advance(ci);
     }
     const int nvalid = cursor_valid(cc);
     advance(cc);
     Frags<D> f;
-    read_frags(k % NBUF, f);
+    read_frags(sc, f);
     attend_tile<D, QT>(f, qf, acc, m_run, l_run, p.qk_scale_log2, 0.f, nvalid, g4);
+    return true;
+  };
+  for (int k = 0;; k += NBUF) {
+    if (!step(std::integral_constant<int, 0>{}, k)) break;
+    if (!step(std::integral_constant<int, 1>{}, k + 1)) break;
+    if constexpr (NBUF > 2)
+      if (!step(std::integral_constant<int, 2 % NBUF>{}, k + 2)) break;
+    if constexpr (NBUF > 3)
+      if (!step(std::integral_constant<int, 3 % NBUF>{}, k + 3)) break;
   }
 
   l_run = sum_across_groups(l_run);
@@ -751,7 +845,7 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
   if (rr < p.R) {
     const int t = rr / p.G, gg = rr % p.G;
     const int64_t orow = ((int64_t)item * p.sq + t) * p.Hq + kvh * p.G + gg;
-    store_tile<D>(acc, m_run, l_run, p.v_scale, o_base, p.out_kind, lse_base, orow, p.partial, g4);
+    store_tile<D, TR>(acc, m_run, l_run, p.v_scale, o_base, p.out_kind, lse_base, orow, p.partial, g4);
   }
 }
 
@@ -768,6 +862,7 @@ using KernelFn = void (*)(AttnParams);
 template <int D, int KV, int QT, int MODE>
 KernelFn pick_keys(int RT, int NW) {
   if (RT == 1 && NW == 4) return attn_kernel<D, 1, 4, KV, QT, MODE>;
+  if (RT == 1 && NW == 2) return attn_kernel<D, 1, 2, KV, QT, MODE>;
   if (RT == 1 && NW == 1) return attn_kernel<D, 1, 1, KV, QT, MODE>;
   if (RT == 2 && NW == 2) return attn_kernel<D, 2, 2, KV, QT, MODE>;
   if (RT == 4 && NW == 1) return attn_kernel<D, 4, 1, KV, QT, MODE>;
@@ -836,7 +931,8 @@ hipError_t launch_attention(const AttnParams& p, const LaunchShape& s, int64_t g
   if (!fn) return hipErrorInvalidValue;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * s.NW), 0, stream, p);
+  const size_t lds = s.rows_split ? 0 : merge_lds_bytes(s.D, s.NW, p.R, s.RT);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * s.NW), lds, stream, p);
   return hipGetLastError();
 }
 

@@ -7,11 +7,13 @@
 // weights), output = weighted sum of the live partial outputs.  Split-KV uses
 // it with a zero prior and "live" meaning a finite partial LSE.
 //
-// One wave per (row, head).  Lane s holds the logit of partial s; lanes own
-// head-dim columns d = lane + 64c.  Partial rows are fetched in batches of 8
-// independent loads per lane, issued without waiting for the logits, and a
-// dead partial's row (possibly never written) only ever meets a select, so it
-// cannot leak into the result.
+// One thread per V consecutive head-dim values of one (row, head).  Each
+// thread reads the partial logits itself (the D/V threads of a row share them
+// through the cache), so there is no cross-lane step, and it fetches the
+// partial rows in batches of kBatch independent loads, issued together with
+// the logits.  Batches are merged with a running maximum.  A dead partial's
+// row (possibly never written) only ever meets a select, so it cannot leak
+// into the result.
 
 #include "pa_device.h"
 #include "pa_kernels.h"
@@ -24,113 +26,120 @@ namespace {
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kBatch = 8;
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
-template <int PK>
-__device__ __forceinline__ float load_elem(const void* base, int64_t i) {
-  if constexpr (PK == K_F32) return reinterpret_cast<const float*>(base)[i];
-  const uint16_t b = reinterpret_cast<const uint16_t*>(base)[i];
-  if constexpr (PK == K_BF16) return __uint_as_float((uint32_t)b << 16);
-  return (float)bitcast<_Float16>(b);
-}
-
-__device__ __forceinline__ void store_elem(void* base, int64_t i, int kind, float x) {
-  if (kind == K_F32) {
-    reinterpret_cast<float*>(base)[i] = x;
-  } else if (kind == K_BF16) {
-    reinterpret_cast<__bf16*>(base)[i] = (__bf16)x;
-  } else {
-    reinterpret_cast<_Float16*>(base)[i] = (_Float16)x;
-  }
-}
-
-// Merge G partial rows (row g at obase + g * ostride, element kind PK) of one
-// (row, head).  `logit(g)` is the natural-log logit of partial g, -inf if dead.
-// C = ceil(D / 64) head-dim columns per lane.
-template <int C, int PK, typename LogitFn>
-__device__ __forceinline__ void merge_row(int G, int D, LogitFn logit, const void* obase,
-                                          int64_t ostride, void* out, int64_t out_off,
-                                          int out_kind, float* lse, int64_t lse_off) {
-  const int lane = threadIdx.x & 63;
-  float M = kNegInf;
-  for (int g0 = 0; g0 < G; g0 += 64) {
-    const int g = g0 + lane;
-    M = fmaxf(M, g < G ? logit(g) : kNegInf);
-  }
-  M = wave_max(M);
-  float o[C];
-#pragma unroll
-  for (int c = 0; c < C; ++c) o[c] = 0.f;
-  float tot = 0.f;
-  if (M != kNegInf) {
-    for (int g0 = 0; g0 < G; g0 += 64) {
-      const int g = g0 + lane;
-      const float lg = g < G ? logit(g) : kNegInf;
-      const float w_lane = lg == kNegInf ? 0.f : fast_exp2((lg - M) * kLog2e);
-      tot += w_lane;
-      const int n = G - g0 < 64 ? G - g0 : 64;
-      for (int j = 0; j < n; j += kBatch) {
-        float x[kBatch][C];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int gg = g0 + (j + u < n ? j + u : 0);
-#pragma unroll
-          for (int c = 0; c < C; ++c) {
-            const int d = lane + 64 * c;
-            x[u][c] = d < D ? load_elem<PK>(obase, (int64_t)gg * ostride + d) : 0.f;
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const float w = __shfl(w_lane, j + u < n ? j + u : 0, 64);
-          const bool use = (j + u < n) && w > 0.f;
-#pragma unroll
-          for (int c = 0; c < C; ++c) o[c] = use ? o[c] + w * x[u][c] : o[c];
-        }
-      }
+template <int V, int PK>
+__device__ __forceinline__ void load_vec(const void* base, int64_t i, float (&x)[V]) {
+  if constexpr (PK == K_F32) {
+    const float* p = reinterpret_cast<const float*>(base) + i;
+    if constexpr (V == 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+      x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
+    } else {
+      x[0] = *p;
     }
-    tot = wave_sum(tot);
-    const float inv = 1.f / tot;
+  } else {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + i;
+    uint16_t b[V];
+    if constexpr (V == 4) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+      b[0] = (uint16_t)w[0]; b[1] = (uint16_t)(w[0] >> 16);
+      b[2] = (uint16_t)w[1]; b[3] = (uint16_t)(w[1] >> 16);
+    } else {
+      b[0] = *p;
+    }
 #pragma unroll
-    for (int c = 0; c < C; ++c) o[c] *= inv;
+    for (int i2 = 0; i2 < V; ++i2)
+      x[i2] = PK == K_BF16 ? __uint_as_float((uint32_t)b[i2] << 16) : (float)bitcast<_Float16>(b[i2]);
   }
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const int d = lane + 64 * c;
-    if (d < D) store_elem(out, out_off + d, out_kind, o[c]);
-  }
-  if (lse && lane == 0) lse[lse_off] = tot > 0.f ? M + logf(tot) : kNegInf;
 }
 
-template <int C>
+template <int V>
+__device__ __forceinline__ void store_vec(void* base, int64_t i, int kind, const float (&x)[V]) {
+  if constexpr (V == 4) {
+    store_row<4>(base, i, kind, x);
+  } else if (kind == K_F32) {
+    reinterpret_cast<float*>(base)[i] = x[0];
+  } else if (kind == K_BF16) {
+    reinterpret_cast<__bf16*>(base)[i] = (__bf16)x[0];
+  } else {
+    reinterpret_cast<_Float16*>(base)[i] = (_Float16)x[0];
+  }
+}
+
+// Merge G partials of one (row, head) for this thread's V values.  logit(g)
+// is the natural-log logit of partial g (-inf: dead); load(g, x) fetches its
+// values.  Returns the weighted mean in o and the merged LSE.
+template <int V, typename LogitFn, typename LoadFn>
+__device__ __forceinline__ float merge_partials(int G, LogitFn logit, LoadFn load, float (&o)[V]) {
+  float m = kNegInf, l = 0.f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) o[i] = 0.f;
+  for (int g0 = 0; g0 < G; g0 += kBatch) {
+    float lg[kBatch], x[kBatch][V];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const bool in = g0 + u < G;
+      const int g = in ? g0 + u : g0;  // past the end: a valid index, weight forced to 0
+      const float lv = logit(g);
+      lg[u] = in ? lv : kNegInf;
+      load(g, x[u]);
+    }
+    float mb = m;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) mb = fmaxf(mb, lg[u]);
+    if (mb == kNegInf) continue;  // every partial so far is dead
+    if (mb > m) {
+      const float a = fast_exp2((m - mb) * kLog2e);  // 0 while m is still -inf
+      l *= a;
+#pragma unroll
+      for (int i = 0; i < V; ++i) o[i] *= a;
+      m = mb;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float w = lg[u] == kNegInf ? 0.f : fast_exp2((lg[u] - m) * kLog2e);
+      l += w;
+#pragma unroll
+      for (int i = 0; i < V; ++i) o[i] = w > 0.f ? o[i] + w * x[u][i] : o[i];
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) o[i] *= inv;
+  return l > 0.f ? m + logf(l) : kNegInf;
+}
+
+template <int V>
 __global__ __launch_bounds__(256) void split_combine_kernel(const float* __restrict__ part_o,
                                                             const float* __restrict__ part_lse,
                                                             int32_t S, int32_t rows, int32_t Hq,
                                                             int32_t D, void* out, int32_t out_kind,
                                                             float* lse) {
-  const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // row * Hq + head
   const int64_t total = (int64_t)rows * Hq;
+  const int tpr = D / V;  // threads per (row, head)
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rh = t / tpr;  // row * Hq + head
   if (rh >= total) return;
+  const int d0 = (int)(t - rh * tpr) * V;
   auto logit = [&](int s) -> float { return part_lse[(int64_t)s * total + rh]; };
-  merge_row<C, K_F32>(S, D, logit, part_o + rh * D, total * D, out, rh * D, out_kind, lse, rh);
+  auto load = [&](int s, float (&x)[V]) {
+    load_vec<V, K_F32>(part_o, ((int64_t)s * total + rh) * D + d0, x);
+  };
+  float o[V];
+  const float L = merge_partials<V>(S, logit, load, o);
+  store_vec<V>(out, rh * D + d0, out_kind, o);
+  if (lse && d0 == 0) lse[rh] = L;
 }
 
-template <int C, int PK>
+template <int V, int PK>
 __global__ __launch_bounds__(256) void segment_combine_kernel(
     const void* __restrict__ part_o, const float* __restrict__ part_lse,
     const int32_t* __restrict__ used, const float* __restrict__ bias, int32_t N, int32_t G,
     int32_t Hq, int32_t D, void* out, int32_t out_kind, float* lse) {
-  const int64_t nh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // n * Hq + h
+  const int tpr = D / V;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nh = t / tpr;  // n * Hq + h
   if (nh >= (int64_t)N * Hq) return;
+  const int d0 = (int)(t - nh * tpr) * V;
   const int64_t n = nh / Hq;
   const int h = (int)(nh - n * Hq);
   auto logit = [&](int g) -> float {
@@ -138,9 +147,13 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(
     const float prior = g < G - 1 ? bias[n * (G - 1) + g] : 0.f;
     return part_lse[(n * G + g) * Hq + h] + prior;
   };
-  const int64_t eb = PK == K_F32 ? 4 : 2;
-  const char* obase = static_cast<const char*>(part_o) + ((n * G) * Hq + h) * D * eb;
-  merge_row<C, PK>(G, D, logit, obase, (int64_t)Hq * D, out, nh * D, out_kind, lse, nh);
+  auto load = [&](int g, float (&x)[V]) {
+    load_vec<V, PK>(part_o, ((n * G + g) * Hq + h) * D + d0, x);
+  };
+  float o[V];
+  const float L = merge_partials<V>(G, logit, load, o);
+  store_vec<V>(out, nh * D + d0, out_kind, o);
+  if (lse && d0 == 0) lse[nh] = L;
 }
 
 __global__ void describe_kernel(const int32_t* __restrict__ table, int64_t bt_stride,
@@ -166,57 +179,66 @@ __global__ void describe_kernel(const int32_t* __restrict__ table, int64_t bt_st
     }
 }
 
-template <int C>
-hipError_t launch_split_c(const float* part_o, const float* part_lse, int32_t S, int32_t rows,
+template <int V>
+hipError_t launch_split_v(const float* part_o, const float* part_lse, int32_t S, int32_t rows,
                           int32_t Hq, int32_t D, void* out, int32_t out_kind, float* lse,
-                          hipStream_t stream, int64_t grid) {
-  hipLaunchKernelGGL(split_combine_kernel<C>, dim3((unsigned)grid), dim3(256), 0, stream, part_o,
+                          hipStream_t stream) {
+  const int64_t threads = (int64_t)rows * Hq * (D / V);
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(split_combine_kernel<V>, dim3((unsigned)grid), dim3(256), 0, stream, part_o,
                      part_lse, S, rows, Hq, D, out, out_kind, lse);
   return hipGetLastError();
 }
 
-template <int C, int PK>
-hipError_t launch_segment_c(const void* part_o, const float* part_lse, const int32_t* used,
+template <int V, int PK>
+hipError_t launch_segment_v(const void* part_o, const float* part_lse, const int32_t* used,
                             const float* bias, int32_t N, int32_t G, int32_t Hq, int32_t D,
-                            void* out, int32_t out_kind, float* lse, hipStream_t stream,
-                            int64_t grid) {
-  hipLaunchKernelGGL((segment_combine_kernel<C, PK>), dim3((unsigned)grid), dim3(256), 0, stream,
+                            void* out, int32_t out_kind, float* lse, hipStream_t stream) {
+  const int64_t threads = (int64_t)N * Hq * (D / V);
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((segment_combine_kernel<V, PK>), dim3((unsigned)grid), dim3(256), 0, stream,
                      part_o, part_lse, used, bias, N, G, Hq, D, out, out_kind, lse);
   return hipGetLastError();
 }
+
+// Four values per thread when the rows allow whole-vector accesses.
+bool vec4_ok(const void* in, int in_bytes, const void* out, int out_bytes, int D) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(in), b = reinterpret_cast<uintptr_t>(out);
+  return D % 4 == 0 && a % (4 * in_bytes) == 0 && b % (4 * out_bytes) == 0;
+}
+
+int elem_bytes(int kind) { return kind == K_F32 ? 4 : 2; }
 
 }  // namespace
 
 hipError_t launch_split_combine(const float* part_o, const float* part_lse, int32_t S,
                                 int32_t rows, int32_t Hq, int32_t D, void* out, int32_t out_kind,
                                 float* lse, hipStream_t stream) {
-  const int64_t waves = (int64_t)rows * Hq;
-  if (waves == 0) return hipSuccess;
-  const int64_t grid = (waves + 3) / 4;
-  if (D <= 64) return launch_split_c<1>(part_o, part_lse, S, rows, Hq, D, out, out_kind, lse, stream, grid);
-  if (D <= 128) return launch_split_c<2>(part_o, part_lse, S, rows, Hq, D, out, out_kind, lse, stream, grid);
-  return launch_split_c<4>(part_o, part_lse, S, rows, Hq, D, out, out_kind, lse, stream, grid);
+  if ((int64_t)rows * Hq == 0) return hipSuccess;
+  if (vec4_ok(part_o, 4, out, elem_bytes(out_kind), D))
+    return launch_split_v<4>(part_o, part_lse, S, rows, Hq, D, out, out_kind, lse, stream);
+  return launch_split_v<1>(part_o, part_lse, S, rows, Hq, D, out, out_kind, lse, stream);
 }
 
 hipError_t launch_segment_combine(const void* part_o, int32_t part_kind, const float* part_lse,
                                   const int32_t* used, const float* bias, int32_t N, int32_t G,
                                   int32_t Hq, int32_t D, void* out, int32_t out_kind, float* lse,
                                   hipStream_t stream) {
-  const int64_t waves = (int64_t)N * Hq;
-  if (waves == 0) return hipSuccess;
-  const int64_t grid = (waves + 3) / 4;
-#define PA_SEG(C)                                                                                \
-  if (part_kind == K_F32)                                                                        \
-    return launch_segment_c<C, K_F32>(part_o, part_lse, used, bias, N, G, Hq, D, out, out_kind, \
-                                      lse, stream, grid);                                       \
-  if (part_kind == K_BF16)                                                                       \
-    return launch_segment_c<C, K_BF16>(part_o, part_lse, used, bias, N, G, Hq, D, out, out_kind,\
-                                       lse, stream, grid);                                      \
-  return launch_segment_c<C, K_FP16>(part_o, part_lse, used, bias, N, G, Hq, D, out, out_kind,  \
-                                     lse, stream, grid);
-  if (D <= 64) { PA_SEG(1) }
-  if (D <= 128) { PA_SEG(2) }
-  PA_SEG(4)
+  if ((int64_t)N * Hq == 0) return hipSuccess;
+  const bool v4 = vec4_ok(part_o, elem_bytes(part_kind), out, elem_bytes(out_kind), D);
+#define PA_SEG(V)                                                                                 \
+  if (part_kind == K_F32)                                                                         \
+    return launch_segment_v<V, K_F32>(part_o, part_lse, used, bias, N, G, Hq, D, out, out_kind, \
+                                      lse, stream);                                              \
+  if (part_kind == K_BF16)                                                                        \
+    return launch_segment_v<V, K_BF16>(part_o, part_lse, used, bias, N, G, Hq, D, out, out_kind,\
+                                       lse, stream);                                             \
+  return launch_segment_v<V, K_FP16>(part_o, part_lse, used, bias, N, G, Hq, D, out, out_kind,  \
+                                     lse, stream);
+  if (v4) { PA_SEG(4) }
+  PA_SEG(1)
 #undef PA_SEG
 }
 

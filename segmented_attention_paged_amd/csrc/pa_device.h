@@ -81,16 +81,22 @@ __device__ __forceinline__ uint32_t lo_lo(uint32_t a, uint32_t b) { return (a & 
 __device__ __forceinline__ uint32_t hi_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
 
 // Reductions across the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48).
-__device__ __forceinline__ float max_across_groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  x = fmaxf(x, __shfl_xor(x, 32, 64));
-  return x;
+// gfx950 lane swaps: permlane32_swap(a, b) exchanges lanes 32..63 of a with
+// lanes 0..31 of b; permlane16_swap(a, b) exchanges the odd 16-lane rows of a
+// with the even rows of b.  Called with a == b == x, element-wise op of the
+// two results is op(x[l], x[l ^ 32]) (resp. x[l ^ 16]) in every lane.
+__device__ __forceinline__ float xor32_pair(float x, bool max_op) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return max_op ? fmaxf(a, b) : a + b;
 }
-__device__ __forceinline__ float sum_across_groups(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
+__device__ __forceinline__ float xor16_pair(float x, bool max_op) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return max_op ? fmaxf(a, b) : a + b;
 }
+__device__ __forceinline__ float max_across_groups(float x) { return xor32_pair(xor16_pair(x, true), true); }
+__device__ __forceinline__ float sum_across_groups(float x) { return xor32_pair(xor16_pair(x, false), false); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -46,6 +46,17 @@ struct LaunchShape {
   int D, kv_kind, q_kind, RT, NW, mode, rows_split;
 };
 
+// Rows of attn_kernel's cross-wave merge buffer: a workgroup holds `rows` query
+// rows (RT * 16) of which only the first R exist when R is smaller.
+__host__ __device__ inline int merge_rows(int R, int rows) { return R < rows ? R : rows; }
+
+// Dynamic LDS bytes of attn_kernel's merge (fp32 O rows padded to D + 4, then m and l).
+inline size_t merge_lds_bytes(int D, int NW, int R, int RT) {
+  if (NW <= 1) return 0;
+  const size_t rr = (size_t)merge_rows(R, RT * 16);
+  return (size_t)NW * rr * (size_t)(D + 4) * 4 + 2 * (size_t)NW * rr * 4;
+}
+
 // 1 KiB direct-to-LDS loads per staged tile (the shared kernel needs NW to divide it).
 int shared_tile_loads(int D, int kv_kind);
 

@@ -90,6 +90,10 @@ def test_auto_splits_are_valid():
         ws = sap.workspace_size(*shape[:7], window=shape[7], num_splits=0)
         assert (ws == 0) == (S == 1)
     assert sap.resolve_splits(8, 1, 64, 8, 128, 16, 8192, 0, 16) == 16
+    # automatic policy at the measured shapes: decode 4, query block 8 (4 with a 4096 window)
+    assert sap.resolve_splits(64, 1, 32, 8, 128, 16, 512, 0, 0) == 4
+    assert sap.resolve_splits(32, 16, 32, 8, 128, 16, 2048, 0, 0) == 8
+    assert sap.resolve_splits(32, 16, 32, 8, 128, 16, 2048, 4096, 0) == 4
     assert sap.resolve_splits(2, 1, 4, 1, 64, 16, 7, 0, 0) == 1
 
 
