@@ -58,7 +58,9 @@ enum pa_status {
  * module docstring: the only layout requirement).  For vLLM's
  * [pages, Hkv, P, 2*D] page, v = k + D and the strides are
  * (Hkv*P*2D, P*2D, 2D).  k, v must be 16-byte aligned and every stride a
- * multiple of 16 bytes.  Page indices read from the block table are clamped
+ * multiple of 16 bytes, one token step (token_stride elements) at most 64 MiB
+ * (PA_EINVAL otherwise).
+ * Page indices read from the block table are clamped
  * to [0, num_pages) so a corrupt table cannot address outside the pool. */
 typedef struct pa_kv_desc {
   const void* k;
@@ -74,7 +76,8 @@ typedef struct pa_kv_desc {
   float v_scale;        /* real V = v_scale * stored V (1 unless fp8) */
 } pa_kv_desc;
 
-/* Paged attention of a uniform query block: A1..A10 of the path.
+/* Paged attention of a uniform query block: work partition, window restriction,
+ * block-table gather, attention, and the split combine when splits > 1.
  *
  * q           [B, query_len, Hq, D] contiguous, q_dtype PA_BF16 | PA_FP16.
  *             A 16-bit cache must have the query's dtype; an fp8 cache takes
@@ -149,7 +152,7 @@ int paged_attn_partial(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
                        int32_t D, float scale, int32_t window, int32_t num_splits,
                        float* part_o, float* part_lse, hipStream_t stream);
 
-/* Split-KV combine (A10).  For each row r < rows and head h < Hq:
+/* Split-KV combine.  For each row r < rows and head h < Hq:
  *   LSE = ln sum_{live s} exp(part_lse[s]);  O = sum_{live s} exp(part_lse[s] - LSE) part_o[s]
  * with live meaning part_lse[s] > -inf; no live split gives O = 0, LSE = -inf.
  * This is the segment combine of the dash_attention page with zero bias.
@@ -159,7 +162,7 @@ int split_kv_combine(const float* part_o, const float* part_lse, int32_t S, int3
                      int32_t Hq, int32_t D, void* out, int32_t out_dtype, float* lse,
                      hipStream_t stream);
 
-/* DASH segment combine (A12; dash_attention page, flash_dash_attention).
+/* DASH segment combine (dash_attention page, flash_dash_attention).
  * For each query n and head h, with prior_g = bias[n, g] for g < G-1 and 0
  * for the last (local) segment, and live_g = used[n, g] > 0:
  *   w = softmax over live g of (part_lse[n, g, h] + prior_g)   (all dead: w = 0)
@@ -173,7 +176,7 @@ int segment_attn_combine(const void* part_o, int32_t part_dtype, const float* pa
                          int32_t Hq, int32_t D, void* out, int32_t out_dtype, float* lse,
                          hipStream_t stream);
 
-/* DASH segmented attention (A11 + A12; dash_attention page, flash_dash_attention).
+/* DASH segmented attention and its combine (dash_attention page, flash_dash_attention).
  * q [N, Hq, D]; k, v contiguous [N*(topk*bs+local), Hkv, D] in kv_dtype (same
  * 16-bit type as q); per query the rows hold topk remote segments of bs rows
  * and then one local segment of `local` rows.  used [N, topk+1] int32: the

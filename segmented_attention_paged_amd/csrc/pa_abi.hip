@@ -137,6 +137,8 @@ int check_paged(const void* q, int32_t q_dtype, const pa_kv_desc* kv, const int3
   if ((kv->page_stride * eb) % 16 || (kv->head_stride * eb) % 16 || (kv->token_stride * eb) % 16 ||
       kv->page_stride < 0 || kv->head_stride < 0 || kv->token_stride <= 0)
     return fail(PA_EINVAL, "kv strides must be non-negative multiples of 16 bytes");
+  if (kv->token_stride * eb > (int64_t)1 << 26)  // lane offsets inside a tile are 32-bit
+    return fail(PA_EINVAL, "token stride above 64 MiB");
   if (B == 0 || query_len == 0) return PA_OK;
   if (!q || !kv->k || !kv->v || !block_table || !seq_lens)
     return fail(PA_EINVAL, "NULL input pointer");
@@ -354,6 +356,7 @@ int segment_attn_run(const void* q, int32_t q_dtype, const void* k, const void* 
   if (N < 0 || topk < 0 || topk > 63) return fail(PA_EINVAL, "bad N or topk");
   if (D != 64 && D != 128) return fail(PA_EINVAL, "head_dim must be 64 or 128");
   if (Hkv <= 0 || Hq <= 0 || Hq % Hkv) return fail(PA_EINVAL, "Hq must be a positive multiple of Hkv");
+  if ((int64_t)Hkv * D * 2 > (int64_t)1 << 26) return fail(PA_EINVAL, "token stride above 64 MiB");
   if (out_dtype != PA_BF16 && out_dtype != PA_FP16 && out_dtype != PA_F32)
     return fail(PA_ENOTSUP, "out dtype must be bf16, fp16 or f32");
   if (!std::isfinite(scale)) return fail(PA_EINVAL, "scale must be finite");

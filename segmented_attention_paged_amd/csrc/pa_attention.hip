@@ -65,6 +65,14 @@ struct TileInfo {
   float bias;      // log2-domain logit bias of the tile (fused segments)
 };
 
+// Copy of a wave-uniform 64-bit value in scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint64_t a = (uint64_t)x;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // K/V bytes are read exactly once per launch: non-temporal loads keep them
 // from displacing anything in the caches (measured +14% on random 8 KiB pages).
 __device__ __forceinline__ u32x4 stream_load16(const char* src) {
@@ -459,16 +467,21 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
     return ti;
   };
 
+  // Tile bases are wave-uniform (scalar registers); lanes add 32-bit offsets,
+  // so each load is a scalar base plus one VGPR offset.
+  const uint32_t tsb = (uint32_t)ts_b;  // 16 * tsb < 2^31 (checked at the boundary)
   auto load_tile = [&](Raw<D, KV>& r, const TileInfo& ti) {
-    const int ks = c16 < ti.nvalid ? c16 : 0;  // invalid slots read slot 0 (masked later)
-    const char* kl = ti.kp + ks * ts_b + 16 * g4;
+    // offsets from the kernel-argument pointers keep the global address space
+    const char* kb = p.k + uniform64(ti.kp - p.k);
+    const char* vb = p.k + uniform64(ti.vp - p.k);
+    const uint32_t ks = c16 < ti.nvalid ? c16 : 0;  // invalid slots read slot 0 (masked later)
+    const uint32_t koff = ks * tsb + 16 * g4;
 #pragma unroll
-    for (int i = 0; i < G::KLD; ++i) r.k[i] = stream_load16(kl + 64 * i);
+    for (int i = 0; i < G::KLD; ++i) r.k[i] = stream_load16(kb + (koff + 64 * i));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int vs = 4 * g4 + i;
-      vs = vs < ti.nvalid ? vs : 0;
-      load_v<G::VDW>(r.v[i], ti.vp + vs * ts_b + G::VB * c16);
+      const uint32_t vs = 4 * g4 + i < ti.nvalid ? 4 * g4 + i : 0;
+      load_v<G::VDW>(r.v[i], vb + (vs * tsb + G::VB * c16));
     }
   };
 
