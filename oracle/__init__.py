@@ -34,6 +34,13 @@ Pinning status of each function (the pins live in tests/test_oracle_*.py):
       unsplit attention)
   attention.segment_partials / combine_segments ... pinned (union closed form,
       dead-segment invariance, plain attention when every segment is full)
+  cache_write.e4m3fn_encode ....................... pinned (torch float8_e4m3fn
+      cast on finite in-range values, round trip of every finite code, hand
+      ties and saturation points)
+  cache_write.write_kv_cache ...................... pinned (write then paged
+      attention == plain attention over the written rows, padding and
+      out-of-pool slots write nothing, order independence); the readings it
+      follows where the page is silent are listed in its module docstring
 """
 
 from .formats import bf16_to_f64, fp16_to_f64, e4m3fn_to_f64, e4m3fn_value, E4M3FN_TABLE  # noqa: F401
@@ -55,3 +62,4 @@ from .attention import (  # noqa: F401
     segment_attention,
     segment_attention_union,
 )
+from .cache_write import e4m3fn_encode, quantize_e4m3fn, write_kv_cache  # noqa: F401

@@ -8,9 +8,11 @@ no dot products, no softmax, no window or split rule.
 from .gen import (  # noqa: F401
     PagedInputs,
     SegmentInputs,
+    KVWriteInputs,
     CONFIGS,
     make_paged,
     make_segments,
+    make_kv_write,
     paged_config,
     segment_config,
     to_numpy_bits,

@@ -360,6 +360,77 @@ CONFIGS = {
 }
 
 
+@dataclass
+class KVWriteInputs:
+    """New K/V rows of T tokens and the page cache they are written into."""
+
+    name: str
+    T: int
+    Hkv: int
+    D: int
+    P: int
+    pages: int
+    in_dtype: str  # "bf16" or "fp16"
+    cache_dtype: str  # in_dtype or "fp8_e4m3"
+    k_scale: float
+    v_scale: float
+    key: torch.Tensor  # [T, Hkv, D] in_dtype
+    value: torch.Tensor  # [T, Hkv, D] in_dtype
+    cache: torch.Tensor  # [pages, Hkv, P, 2*D] (uint8 bytes for fp8): contents before the write
+    slot_mapping: torch.Tensor  # [T] int64, distinct slots; -1 = padding token
+
+
+def make_kv_write(*, T: int, Hkv: int, D: int, P: int, pages: int, seed: int,
+                  in_dtype: str = "bf16", cache_dtype: str = "bf16", pad_frac: float = 0.0,
+                  value_scale: float = 1.0, name: str = "kv_write",
+                  device=None) -> KVWriteInputs:
+    """Draw one cache-write workload.
+
+    Order: key -> value -> prior cache contents -> slot permutation -> padding
+    mask -> fp8 scales.  key and value are N(0, 1) * value_scale rounded to the
+    input type; the prior cache holds N(0, 1) values (random bytes for fp8);
+    the T tokens take distinct slots drawn uniformly from the pool's
+    pages * P slots (T <= pages * P); a fraction pad_frac of them is -1.
+    With ``device`` set to a GPU, key, value and the cache are drawn there by a
+    second generator seeded with ``seed + DEVICE_SEED_OFFSET``.
+    """
+    if T > pages * P:
+        raise ValueError("more tokens than slots")
+    g = torch.Generator().manual_seed(int(seed))
+    gd = g
+    if device is not None and torch.device(device).type != "cpu":
+        gd = torch.Generator(device=device).manual_seed(int(seed) + DEVICE_SEED_OFFSET)
+    tdt = torch.float16 if in_dtype == "fp16" else torch.bfloat16
+
+    def draw(shape):
+        out = torch.empty(tuple(shape), dtype=tdt, device=gd.device)
+        per_row = max(1, out[0].numel()) if out.numel() else 1
+        rows = max(1, _CHUNK_VALUES // per_row)
+        for r0 in range(0, out.shape[0], rows):
+            r1 = min(out.shape[0], r0 + rows)
+            x = torch.randn((r1 - r0,) + tuple(shape[1:]), generator=gd, device=gd.device)
+            out[r0:r1] = (x * value_scale).to(tdt)
+        return out
+
+    key = draw((T, Hkv, D))
+    value = draw((T, Hkv, D))
+    if cache_dtype == "fp8_e4m3":
+        cache = torch.randint(0, 256, (pages, Hkv, P, 2 * D), generator=gd, device=gd.device,
+                              dtype=torch.int32).to(torch.uint8)
+    else:
+        cache = draw((pages, Hkv, P, 2 * D))
+    slots = torch.randperm(pages * P, generator=g)[:T].to(torch.int64)
+    pad = torch.rand(T, generator=g) < pad_frac
+    slots = torch.where(pad, torch.full_like(slots, -1), slots)
+    k_scale = v_scale = 1.0
+    if cache_dtype == "fp8_e4m3":
+        k_scale = float(0.5 + 1.5 * torch.rand((), generator=g, dtype=torch.float64))
+        v_scale = float(0.5 + 1.5 * torch.rand((), generator=g, dtype=torch.float64))
+    return KVWriteInputs(name=name, T=T, Hkv=Hkv, D=D, P=P, pages=pages, in_dtype=in_dtype,
+                         cache_dtype=cache_dtype, k_scale=k_scale, v_scale=v_scale, key=key,
+                         value=value, cache=cache, slot_mapping=slots.to(gd.device))
+
+
 def paged_config(name: str, poison: bool = False, device=None) -> PagedInputs:
     cfg = dict(CONFIGS[name])
     if cfg.pop("kind") != "paged":
