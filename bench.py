@@ -12,7 +12,11 @@ attention partial pass) is also timed alone, in the same launch
 configuration, with HIP events on the launch stream; its algorithmic bytes
 per launch are the visible K/V bytes: sum_b L'_b * Hkv * 2 * D * 2.
 
-    python bench.py [--steps K] [--warmup W] [--all] [--no-cpu-baseline]
+The "kv_write" entry times paged_kv_write (new K/V rows scattered into the
+page cache, bf16 and fp8) for a 65536-token prefill chunk and a 64-token
+decode step; its bytes are the rows read plus the slot rows written.
+
+    python bench.py [--steps K] [--warmup W] [--all] [--no-cpu-baseline] [--no-kv-write]
 """
 
 from __future__ import annotations
@@ -231,6 +235,34 @@ def run_segments(steps, warmup):
     return res
 
 
+def run_kv_write(steps, warmup):
+    """paged_kv_write of a prefill chunk (65536 tokens x 8 kv heads x D=128, scattered
+    over a pool of twice as many 16-token slots) and of one decode step (64 tokens)."""
+    import torch
+
+    import segmented_attention_paged_amd as sap
+    from workloads import make_kv_write
+
+    res = {}
+    for cache_dtype in ("bf16", "fp8_e4m3"):
+        for label, T, pages in (("prefill_chunk", 65536, 8192), ("decode_step", 64, 8192)):
+            w = make_kv_write(T=T, Hkv=8, D=128, P=16, pages=pages, seed=50, cache_dtype=cache_dtype,
+                              device="cuda")
+            k, v = sap.kv_halves(w.cache, w.D)
+            fn = lambda: sap.paged_kv_write(w.key, w.value, w.slot_mapping, k, v, k_scale=w.k_scale,
+                                            v_scale=w.v_scale)
+            ms, _ = time_events(fn, steps, warmup)
+            eb = 1 if cache_dtype == "fp8_e4m3" else 2
+            nbytes = T * w.Hkv * w.D * 2 * 2 + T * w.Hkv * 2 * w.D * eb + T * 8  # read, write, slots
+            res[f"{label}_{cache_dtype}"] = {
+                "tokens": T, "us": ms * 1e3, "gbps": nbytes / ms / 1e6,
+                "hbm_frac": nbytes / ms / 1e6 / HBM_PEAK_GBPS, "algorithmic_bytes": nbytes}
+            log(f"kv write {label} {cache_dtype}: {ms * 1e3:.1f} us, {nbytes / ms / 1e6:.0f} GB/s")
+            del w, k, v
+            torch.cuda.empty_cache()
+    return res
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -242,6 +274,7 @@ def main(argv=None) -> int:
     ap.add_argument("--all", action="store_true", help="also time every other workload")
     ap.add_argument("--no-block", action="store_true", help="skip the sq=16 MFMA measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kv-write", action="store_true", help="skip the cache-write measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args(argv)
@@ -326,6 +359,9 @@ def main(argv=None) -> int:
         log(f"c3_query_block: {ms * 1e3:.1f} us, MFMA {bb.flops / ms / 1e9:.1f} TFLOP/s")
         del bb
         torch.cuda.empty_cache()
+
+    if not args.no_kv_write:
+        result["kv_write"] = run_kv_write(max(10, args.steps // 2), max(3, args.warmup // 2))
 
     if args.all:
         extra = {}

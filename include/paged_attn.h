@@ -226,6 +226,31 @@ int paged_attn_describe_host(const int32_t* block_table, int64_t bt_row_stride,
                              int32_t* out_lens, int32_t* out_table, int32_t out_width,
                              int32_t* split_ranges);
 
+/* Paged K/V cache write (flashinfer_ts page, do_kv_cache_update: the new
+ * key and value rows of each token go to its slot of the page cache).
+ *
+ * key, value  [T, Hkv, D] of in_dtype (PA_BF16 | PA_FP16); head rows are
+ *             contiguous, tokens key_token_stride / value_token_stride
+ *             elements apart (multiples of 16 bytes, >= Hkv*D).
+ * slot_mapping [T] int64: token t goes to slot slot_mapping[t] % P of page
+ *             slot_mapping[t] / P.  A negative slot (padding) and a slot at
+ *             or past num_pages*P write nothing.  Slots of one call must be
+ *             distinct (with repeats, which token lands there is unspecified).
+ * cache       the pa_kv_desc of the read side; its k and v memory is WRITTEN
+ *             (K rows into k, V rows into v, so for vLLM's [pages, Hkv, P, 2D]
+ *             page the two halves of each slot row).  dtype = in_dtype (bits
+ *             copied) or PA_FP8_E4M3: stored = e4m3fn(x / k_scale) for K and
+ *             e4m3fn(x / v_scale) for V, the quotient rounded to fp32, then to
+ *             the nearest finite e4m3fn value, ties to even, saturating at
+ *             +-448, NaN kept; k_scale, v_scale > 0 and finite.
+ * D           multiple of 8 in [8, 256].
+ * Async on `stream`; nothing else is read or written.  Errors: PA_ENOTSUP
+ * (dtype combination), PA_EINVAL (geometry, strides, alignment, scales,
+ * NULL pointers when T > 0), PA_EHIP.  T == 0 is a no-op. */
+int paged_kv_write(const void* key, int64_t key_token_stride, const void* value,
+                   int64_t value_token_stride, int32_t in_dtype, int32_t T, int32_t D,
+                   const int64_t* slot_mapping, const pa_kv_desc* cache, hipStream_t stream);
+
 /* Thread-local message describing the last failing call ("" if none). */
 const char* pa_last_error(void);
 

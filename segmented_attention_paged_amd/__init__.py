@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     paged_attn_describe_host,
     paged_attn_partial,
     paged_attn_run,
+    paged_kv_write,
     plan,
     resolve_splits,
     segment_attn_combine,

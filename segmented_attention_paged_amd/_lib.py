@@ -50,7 +50,8 @@ SIGNATURES = {
                                       _f32, _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),
     "paged_attn_resolve_splits": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "paged_attn_plan": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
-    "paged_attn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),    "paged_attn_partial": (ctypes.c_int, [_vp, _i32, _kvp, _vp, _i64, _i32, _vp, _i32, _i32, _i32,
+    "paged_attn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "paged_attn_partial": (ctypes.c_int, [_vp, _i32, _kvp, _vp, _i64, _i32, _vp, _i32, _i32, _i32,
                                           _i32, _f32, _i32, _i32, _vp, _vp, _vp]),
     "split_kv_combine": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]),
     "segment_attn_combine": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp,
@@ -63,6 +64,7 @@ SIGNATURES = {
                                            _i32, _i32, _vp, _vp, _i32, _vp, _vp]),
     "paged_attn_describe_host": (ctypes.c_int, [_vp, _i64, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                                 _i32, _i32, _i32, _vp, _vp, _i32, _vp]),
+    "paged_kv_write": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp, _kvp, _vp]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_version": (ctypes.c_char_p, []),
 }

@@ -192,6 +192,26 @@ def segment_attn_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, used: to
     return out, lse
 
 
+def paged_kv_write(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,
+                   k: torch.Tensor, v: torch.Tensor, *, k_scale: float = 1.0,
+                   v_scale: float = 1.0) -> None:
+    """Write token rows key[t], value[t] ([T, Hkv, D]) into slot slot_mapping[t] of the
+    paged cache views k, v ([pages, Hkv, page_size, D], e.g. kv_halves of the cache).
+    An fp8 (uint8 / float8_e4m3fn) cache stores e4m3fn(x / k_scale), e4m3fn(x / v_scale)."""
+    if key.shape != value.shape or key.dim() != 3:
+        raise ValueError("key and value must both be [T, Hkv, D]")
+    if key.stride(1) != key.shape[2] or key.stride(2) != 1 or value.stride(1) != value.shape[2] \
+            or value.stride(2) != 1:
+        raise ValueError("key and value rows must be head-contiguous")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1 or slot_mapping.shape[0] != key.shape[0]:
+        raise ValueError("slot_mapping must be int64 [T]")
+    desc = kv_desc(k, v, k_scale=k_scale, v_scale=v_scale)
+    T, _, D = key.shape
+    check(load().paged_kv_write(key.data_ptr(), key.stride(0), value.data_ptr(), value.stride(0),
+                                dtype_code(key.dtype), T, D, slot_mapping.contiguous().data_ptr(),
+                                ctypes.byref(desc), _stream(key.device)))
+
+
 def window_width(window: int, query_len: int, page_size: int, bt_width: int) -> int:
     return int(load().paged_attn_window_width(window, query_len, page_size, bt_width))
 

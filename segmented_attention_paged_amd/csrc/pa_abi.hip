@@ -481,4 +481,54 @@ int paged_attn_describe_host(const int32_t* block_table, int64_t bt_row_stride, 
   return ok();
 }
 
+int paged_kv_write(const void* key, int64_t key_token_stride, const void* value,
+                   int64_t value_token_stride, int32_t in_dtype, int32_t T, int32_t D,
+                   const int64_t* slot_mapping, const pa_kv_desc* cache, hipStream_t stream) {
+  if (!cache) return fail(PA_EINVAL, "cache descriptor is NULL");
+  if (in_dtype != PA_BF16 && in_dtype != PA_FP16)
+    return fail(PA_ENOTSUP, "key/value dtype must be bf16 or fp16 (got %d)", in_dtype);
+  if (cache->dtype != in_dtype && cache->dtype != PA_FP8_E4M3)
+    return fail(PA_ENOTSUP, "cache dtype must be the input's or fp8_e4m3 (got %d)", cache->dtype);
+  if (T < 0) return fail(PA_EINVAL, "T must be >= 0");
+  if (D < 8 || D > 256 || D % 8) return fail(PA_EINVAL, "head_dim must be a multiple of 8 in [8, 256]");
+  const int32_t Hkv = cache->num_kv_heads, P = cache->page_size;
+  if (Hkv <= 0 || P <= 0 || cache->num_pages < 0) return fail(PA_EINVAL, "bad cache geometry");
+  if (key_token_stride < (int64_t)Hkv * D || value_token_stride < (int64_t)Hkv * D ||
+      (key_token_stride * 2) % 16 || (value_token_stride * 2) % 16)
+    return fail(PA_EINVAL, "key/value token strides must cover Hkv*D values and be multiples of 16 bytes");
+  const int eb = kind_bytes(cache->dtype);
+  if ((cache->page_stride * eb) % 16 || (cache->head_stride * eb) % 16 || (cache->token_stride * eb) % 16 ||
+      cache->page_stride < 0 || cache->head_stride < 0 || cache->token_stride <= 0)
+    return fail(PA_EINVAL, "cache strides must be non-negative multiples of 16 bytes");
+  if (cache->dtype == PA_FP8_E4M3 &&
+      !(cache->k_scale > 0.f && cache->v_scale > 0.f && std::isfinite(cache->k_scale) &&
+        std::isfinite(cache->v_scale)))
+    return fail(PA_EINVAL, "fp8 cache needs positive finite k_scale and v_scale");
+  if (T == 0 || cache->num_pages == 0) return ok();
+  if (!key || !value || !slot_mapping || !cache->k || !cache->v) return fail(PA_EINVAL, "NULL pointer");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(cache->k) || !aligned16(cache->v))
+    return fail(PA_EINVAL, "key, value and the cache must be 16-byte aligned");
+  KVWriteParams p{};
+  p.key = key;
+  p.value = value;
+  p.key_stride = key_token_stride;
+  p.value_stride = value_token_stride;
+  p.slot_mapping = slot_mapping;
+  p.T = T;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.P = P;
+  p.capacity = (int64_t)cache->num_pages * P;
+  p.k_cache = const_cast<void*>(cache->k);
+  p.v_cache = const_cast<void*>(cache->v);
+  p.page_stride = cache->page_stride;
+  p.head_stride = cache->head_stride;
+  p.token_stride = cache->token_stride;
+  p.k_inv = 1.0 / (double)cache->k_scale;
+  p.v_inv = 1.0 / (double)cache->v_scale;
+  hipError_t e = launch_kv_write(p, in_dtype, cache->dtype, stream);
+  if (e != hipSuccess) return hip_fail(e, "cache write launch");
+  return ok();
+}
+
 }  // extern "C"

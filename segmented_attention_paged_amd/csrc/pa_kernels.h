@@ -74,6 +74,24 @@ hipError_t launch_segment_combine(const void* part_o, int32_t part_kind, const f
                                   int32_t Hq, int32_t D, void* out, int32_t out_kind, float* lse,
                                   hipStream_t stream);
 
+// Paged K/V cache write: token t's rows key[t], value[t] ([Hkv, D] each,
+// head-contiguous) into slot slot_mapping[t] of the cache.
+struct KVWriteParams {
+  const void* key;
+  const void* value;
+  int64_t key_stride;    // elements between tokens of key
+  int64_t value_stride;  // elements between tokens of value
+  const int64_t* slot_mapping;
+  int32_t T, Hkv, D, P;
+  int64_t capacity;      // pages * P
+  void* k_cache;
+  void* v_cache;
+  int64_t page_stride, head_stride, token_stride;  // cache elements
+  double k_inv, v_inv;  // fp8 cache: 1 / k_scale, 1 / v_scale rounded to double
+};
+
+hipError_t launch_kv_write(const KVWriteParams& p, int in_kind, int cache_kind, hipStream_t stream);
+
 hipError_t launch_describe(const int32_t* block_table, int64_t bt_stride, int32_t bt_width,
                            const int32_t* seq_lens, int32_t B, int32_t query_len, int32_t P,
                            int32_t window, int32_t S, int32_t chunk, int32_t* out_lens,
