@@ -29,7 +29,9 @@ Pinning status of each function (the pins live in tests/test_oracle_*.py):
   attention.softmax_attention ..................... pinned (closed forms,
       brute force, torch SDPA in fp64, logaddexp)
   attention.paged_attention ....................... pinned (page permutation,
-      GQA repeat, window suffix, strided vs compact planes, fp8 scale folding)
+      GQA repeat, window suffix, strided vs compact planes, fp8 scale folding;
+      causal mode: brute force, torch SDPA with a boolean mask in fp64, each
+      token == dense decode of the truncated sequence)
   attention.split_partials / combine_splits ....... pinned (identity with
       unsplit attention)
   attention.segment_partials / combine_segments ... pinned (union closed form,

@@ -93,6 +93,7 @@ def paged_attention(
     requests=None,
     kv_heads=None,
     token_range=None,
+    causal: bool = False,
 ):
     """Attention of a uniform query block over a paged cache.
 
@@ -105,6 +106,12 @@ def paged_attention(
     ``token_range(b, start, L) -> (lo, hi)`` optionally narrows the keys
     (used for Split-KV partials).  Returns O [B, sq, Hq, D] and LSE
     [B, sq, Hq] in fp64; entries of requests / kv heads not asked for are NaN.
+
+    causal (flashinfer_ts ``_get_plan``: ``mask_type="causal"`` with
+    ``window_left = window - 1``; ``build`` skips the page restriction then):
+    the block's tokens sit at positions L - sq + t, token t sees keys
+    j <= L - sq + t and, with a window, j >= L - sq + t - (window - 1): an
+    exact per-token window of ``window`` keys ending at the token itself.
     """
     qv = decode(q, q_dtype)
     B, sq, Hq, D = qv.shape
@@ -118,16 +125,27 @@ def paged_attention(
     heads = range(Hkv) if kv_heads is None else kv_heads
     for b in reqs:
         L = int(seq_lens[b])
-        start = window_start_page(L, window, sq, P) * P
+        start = 0 if causal else window_start_page(L, window, sq, P) * P
         lo, hi = (start, L) if token_range is None else token_range(b, start, L)
         for kvh in heads:
             K, V = _gather_request(k_pages, v_pages, kv_dtype, block_table[b], kvh, lo, hi, P,
                                    k_scale, v_scale)
             hs = slice(kvh * G, (kvh + 1) * G)
-            rows = qv[b, :, hs, :].reshape(sq * G, D)
-            o, lse = softmax_attention(rows, K, V, scale)
-            O[b, :, hs, :] = o.reshape(sq, G, -1)
-            LSE[b, :, hs] = lse.reshape(sq, G)
+            if not causal:
+                rows = qv[b, :, hs, :].reshape(sq * G, D)
+                o, lse = softmax_attention(rows, K, V, scale)
+                O[b, :, hs, :] = o.reshape(sq, G, -1)
+                LSE[b, :, hs] = lse.reshape(sq, G)
+                continue
+            j = np.arange(lo, hi)
+            for t in range(sq):
+                pos = L - sq + t
+                keep = j <= pos
+                if window > 0:
+                    keep &= j >= pos - (window - 1)
+                o, lse = softmax_attention(qv[b, t, hs, :], K[keep], V[keep], scale)
+                O[b, t, hs, :] = o
+                LSE[b, t, hs] = lse
     return O, LSE
 
 

@@ -34,7 +34,7 @@ def brute_attention_row(q, keys, values, scale, key_bias=None):
 
 
 def brute_paged(q, cache, table, lens, *, Hkv, P, D, scale, window=0, dec=float,
-                k_scale=1.0, v_scale=1.0):
+                k_scale=1.0, v_scale=1.0, causal=False):
     """Paged attention by brute force over nested Python lists / numpy arrays.
 
     q[b][t][h][d]; cache[page][kvh][slot][0..2D); table[b][col]; dec decodes
@@ -48,7 +48,7 @@ def brute_paged(q, cache, table, lens, *, Hkv, P, D, scale, window=0, dec=float,
         G = Hq // Hkv
         L = int(lens[b])
         start = 0
-        if window > 0:
+        if window > 0 and not causal:
             # smallest page-aligned start that keeps the last window+sq-1 tokens
             first_needed = L - (window + sq - 1)
             while start + P <= first_needed:
@@ -58,6 +58,10 @@ def brute_paged(q, cache, table, lens, *, Hkv, P, D, scale, window=0, dec=float,
                 kvh = h // G
                 keys, vals = [], []
                 for j in range(start, L):
+                    if causal:
+                        pos = L - sq + t  # the token's own position
+                        if j > pos or (window > 0 and pos - j >= window):
+                            continue
                     page = int(table[b][j // P])
                     row = cache[page][kvh][j % P]
                     keys.append([dec(row[d]) * k_scale for d in range(D)])

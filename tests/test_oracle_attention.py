@@ -125,6 +125,77 @@ def test_matches_torch_sdpa_fp64():
         np.testing.assert_allclose(LSE[b], lse, rtol=0, atol=1e-12)
 
 
+# Causal mask with an exact per-token window --------------------------------
+@pytest.mark.parametrize("window", [0, 1, 3, 9])
+def test_causal_brute_force_loops_agree(window):
+    inp = _tiny(seq_lens=[2, 6, 13], sq=3)
+    O, LSE = _run(inp, causal=True, window=window)
+    q, k, v, bt, lens = _np(inp)
+    res = brute_paged(q.tolist(), to_numpy_bits(inp.cache), bt.tolist(), lens.tolist(),
+                      Hkv=inp.Hkv, P=inp.P, D=inp.D, scale=inp.scale, dec=bf16_bits_to_float,
+                      window=window, causal=True)
+    for (b, t, h), (out, lse) in res.items():
+        np.testing.assert_allclose(O[b, t, h], out, rtol=0, atol=1e-12)
+        assert LSE[b, t, h] == pytest.approx(lse, abs=1e-12)
+
+
+@pytest.mark.parametrize("window", [0, 5])
+def test_causal_matches_torch_sdpa_with_mask_fp64(window):
+    inp = make_paged(B=2, sq=4, Hq=8, Hkv=2, D=16, P=4, seq_lens=[16, 16], seed=22)
+    O, LSE = _run(inp, causal=True, window=window)
+    cache = inp.cache.to(torch.float64)
+    G = inp.Hq // inp.Hkv
+    L, sq = 16, inp.sq
+    pos = torch.arange(sq)[:, None] + (L - sq)
+    j = torch.arange(L)[None, :]
+    allowed = j <= pos
+    if window:
+        allowed &= j >= pos - (window - 1)
+    for b in range(inp.B):
+        kv = cache[inp.block_table[b].long()].permute(1, 0, 2, 3).reshape(inp.Hkv, -1, 2 * inp.D)
+        K = kv[..., : inp.D].repeat_interleave(G, 0)
+        V = kv[..., inp.D:].repeat_interleave(G, 0)
+        qq = inp.q[b].to(torch.float64).permute(1, 0, 2)  # [Hq, sq, D]
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, K, V, attn_mask=allowed,
+                                                               scale=inp.scale)
+        np.testing.assert_allclose(O[b], ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+        s = (inp.scale * qq @ K.transpose(1, 2)).masked_fill(~allowed, float("-inf"))
+        np.testing.assert_allclose(LSE[b], torch.logsumexp(s, -1).permute(1, 0).numpy(),
+                                   rtol=0, atol=1e-12)
+
+
+def test_causal_token_equals_decode_of_truncated_sequence():
+    # token t of a causal block sees exactly what a lone query at its position
+    # sees in a dense decode over the first L - sq + t + 1 keys
+    inp = _tiny(seq_lens=[3, 9, 13], sq=3)
+    O, LSE = _run(inp, causal=True)
+    q, k, v, bt, lens = _np(inp)
+    for t in range(inp.sq):
+        lens_t = lens - (inp.sq - 1 - t)
+        Ot, Lt = oracle.paged_attention(q[:, t:t + 1], "bf16", k, v, "bf16", bt, lens_t,
+                                        scale=inp.scale)
+        np.testing.assert_allclose(O[:, t], Ot[:, 0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(LSE[:, t], Lt[:, 0], rtol=0, atol=1e-12)
+
+
+def test_causal_single_token_is_dense_and_wide_window_is_none():
+    inp = _tiny(seq_lens=[1, 7, 13], sq=1)
+    np.testing.assert_array_equal(_run(inp, causal=True)[0], _run(inp)[0])
+    inp3 = _tiny(seq_lens=[3, 7, 13], sq=3)
+    a, la = _run(inp3, causal=True, window=20)
+    b, lb = _run(inp3, causal=True)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(la, lb)
+
+
+def test_causal_token_before_the_sequence_sees_nothing():
+    # L < sq: the first tokens sit at negative positions and see no key
+    inp = _tiny(seq_lens=[1, 2, 13], sq=3)
+    O, LSE = _run(inp, causal=True)
+    assert np.all(LSE[0, :2] == -np.inf) and np.all(O[0, :2] == 0)
+    assert np.all(np.isfinite(LSE[0, 2])) and np.all(LSE[1, 0] == -np.inf)
+
+
 # P13 ------------------------------------------------------------------------
 def test_lse_matches_logaddexp():
     rng = np.random.default_rng(1)
