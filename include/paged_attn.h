@@ -119,6 +119,21 @@ int paged_attn_run(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
                    void* out, int32_t out_dtype, float* lse,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Causal query block (flashinfer_ts _get_plan: mask_type "causal" with
+ * window_left = window - 1).  Arguments, plan, splits and workspace as
+ * paged_attn_run; only the mask differs.  Token t of request b sits at
+ * position L_b - query_len + t and sees the keys j <= that position; with
+ * window > 0 also j >= position - (window - 1), an exact window of `window`
+ * keys per token (no page rounding: pages before the first key any token of
+ * the block can see are skipped, which changes no result).  A token with no
+ * visible key (L_b < query_len) gets out = 0 and LSE = -inf. */
+int paged_attn_run_causal(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
+                          const int32_t* block_table, int64_t bt_row_stride, int32_t bt_width,
+                          const int32_t* seq_lens, int32_t B, int32_t query_len, int32_t Hq,
+                          int32_t D, float scale, int32_t window, int32_t num_splits,
+                          void* out, int32_t out_dtype, float* lse,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* The split count paged_attn_run resolves num_splits to for this shape (>= 1). */
 int32_t paged_attn_resolve_splits(int32_t B, int32_t query_len, int32_t Hq, int32_t Hkv,
                                   int32_t D, int32_t page_size, int32_t bt_width,

@@ -88,9 +88,12 @@ def paged_attn_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_tabl
                    seq_lens: torch.Tensor, *, scale: float, window: int = 0, num_splits: int = 0,
                    k_scale: float = 1.0, v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
                    out_dtype: Optional[torch.dtype] = None, return_lse: bool = True,
-                   lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+                   lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   causal: bool = False):
     """Attention of q [B, sq, Hq, D] over paged K/V views [pages, Hkv, P, D].
 
+    causal=True: bottom-right causal block with an exact per-token window
+    (paged_attn_run_causal); otherwise the dense block with the page-aligned window.
     Returns (out [B, sq, Hq, D], lse [B, sq, Hq] fp32 natural log, or None)."""
     B, sq, Hq, D = q.shape
     if not q.is_contiguous():
@@ -107,7 +110,8 @@ def paged_attn_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_tabl
     if need and workspace is None:
         workspace = new_workspace(need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    check(load().paged_attn_run(
+    fn = load().paged_attn_run_causal if causal else load().paged_attn_run
+    check(fn(
         q.data_ptr(), dtype_code(q.dtype), ctypes.byref(desc), block_table.data_ptr(),
         block_table.stride(0), W, seq_lens.data_ptr(), B, sq, Hq, D, float(scale), int(window),
         int(num_splits), out.data_ptr(), dtype_code(out.dtype), _ptr(lse), _ptr(workspace), ws_bytes,

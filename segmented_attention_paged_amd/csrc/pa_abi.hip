@@ -232,9 +232,13 @@ static int launch_paged(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
                         const int32_t* block_table, int64_t bt_row_stride, int32_t bt_width,
                         const int32_t* seq_lens, int32_t B, int32_t query_len, int32_t Hq,
                         int32_t D, float scale, int32_t window, const Plan& pl, void* out,
-                        int32_t out_kind, float* lse, bool partial, hipStream_t stream) {
+                        int32_t out_kind, float* lse, bool partial, hipStream_t stream,
+                        bool causal = false) {
   AttnParams p = paged_params(q, kv, block_table, bt_row_stride, bt_width, seq_lens, B, query_len,
                               Hq, scale, window, pl);
+  // causal: the page restriction of the window only skips pages no token can
+  // reach; the kernel applies the exact per-token window of `window` keys
+  p.window_left = (causal && window > 0) ? window - 1 : -1;
   const int64_t rows = (int64_t)B * query_len * Hq;
   p.out = out;
   p.out_kind = out_kind;
@@ -242,7 +246,7 @@ static int launch_paged(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
   p.partial = partial ? 1 : 0;
   p.split_stride_o = rows * D;
   p.split_stride_lse = rows;
-  LaunchShape ls{D, kv->dtype, q_dtype, pl.RT, pl.NW, MODE_PAGED, pl.rows_split};
+  LaunchShape ls{D, kv->dtype, q_dtype, pl.RT, pl.NW, MODE_PAGED, pl.rows_split, causal ? 1 : 0};
   if (pl.rows_split && (shared_tile_loads(D, kv->dtype) % pl.NW) != 0)
     return fail(PA_ENOTSUP, "no shared-tile kernel for this head_dim / dtype / wave count");
   const int64_t grid = (int64_t)B * kv->num_kv_heads * pl.RG * pl.S;
@@ -269,11 +273,12 @@ int paged_attn_partial(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
   return rc == PA_OK ? ok() : rc;
 }
 
-int paged_attn_run(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
-                   const int32_t* block_table, int64_t bt_row_stride, int32_t bt_width,
-                   const int32_t* seq_lens, int32_t B, int32_t query_len, int32_t Hq, int32_t D,
-                   float scale, int32_t window, int32_t num_splits, void* out, int32_t out_dtype,
-                   float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+static int run_paged(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
+                     const int32_t* block_table, int64_t bt_row_stride, int32_t bt_width,
+                     const int32_t* seq_lens, int32_t B, int32_t query_len, int32_t Hq, int32_t D,
+                     float scale, int32_t window, int32_t num_splits, void* out, int32_t out_dtype,
+                     float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                     bool causal) {
   int rc = check_paged(q, q_dtype, kv, block_table, bt_row_stride, bt_width, seq_lens, B, query_len,
                        Hq, D, scale);
   if (rc != PA_OK) return rc;
@@ -285,7 +290,7 @@ int paged_attn_run(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
                             num_splits);
   if (pl.S == 1) {
     rc = launch_paged(q, q_dtype, kv, block_table, bt_row_stride, bt_width, seq_lens, B, query_len,
-                      Hq, D, scale, window, pl, out, out_dtype, lse, false, stream);
+                      Hq, D, scale, window, pl, out, out_dtype, lse, false, stream, causal);
     return rc == PA_OK ? ok() : rc;
   }
   const size_t need = paged_attn_workspace_size(B, query_len, Hq, kv->num_kv_heads, D,
@@ -297,12 +302,33 @@ int paged_attn_run(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
   float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                              align256((int64_t)pl.S * rows * D * 4));
   rc = launch_paged(q, q_dtype, kv, block_table, bt_row_stride, bt_width, seq_lens, B, query_len, Hq,
-                    D, scale, window, pl, part_o, PA_F32, part_lse, true, stream);
+                    D, scale, window, pl, part_o, PA_F32, part_lse, true, stream, causal);
   if (rc != PA_OK) return rc;
   hipError_t e = launch_split_combine(part_o, part_lse, pl.S, (int32_t)(B * query_len), Hq, D, out,
                                       out_dtype, lse, stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ok();
+}
+
+int paged_attn_run(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
+                   const int32_t* block_table, int64_t bt_row_stride, int32_t bt_width,
+                   const int32_t* seq_lens, int32_t B, int32_t query_len, int32_t Hq, int32_t D,
+                   float scale, int32_t window, int32_t num_splits, void* out, int32_t out_dtype,
+                   float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run_paged(q, q_dtype, kv, block_table, bt_row_stride, bt_width, seq_lens, B, query_len, Hq,
+                   D, scale, window, num_splits, out, out_dtype, lse, workspace, workspace_bytes,
+                   stream, false);
+}
+
+int paged_attn_run_causal(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
+                          const int32_t* block_table, int64_t bt_row_stride, int32_t bt_width,
+                          const int32_t* seq_lens, int32_t B, int32_t query_len, int32_t Hq,
+                          int32_t D, float scale, int32_t window, int32_t num_splits, void* out,
+                          int32_t out_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  return run_paged(q, q_dtype, kv, block_table, bt_row_stride, bt_width, seq_lens, B, query_len, Hq,
+                   D, scale, window, num_splits, out, out_dtype, lse, workspace, workspace_bytes,
+                   stream, true);
 }
 
 int split_kv_combine(const float* part_o, const float* part_lse, int32_t S, int32_t rows,
@@ -396,7 +422,7 @@ int segment_attn_run(const void* q, int32_t q_dtype, const void* k, const void* 
     p.out_kind = out_dtype;
     p.lse = lse;
     p.partial = 0;
-    const LaunchShape ls{D, kv_dtype, q_dtype, RT, NW, MODE_SEGMENT_FUSED, 0};
+    const LaunchShape ls{D, kv_dtype, q_dtype, RT, NW, MODE_SEGMENT_FUSED, 0, 0};
     hipError_t e = launch_attention(p, ls, (int64_t)N * Hkv * RG, stream);
     if (e != hipSuccess) return hip_fail(e, "segment attention launch");
     return ok();
@@ -414,7 +440,7 @@ int segment_attn_run(const void* q, int32_t q_dtype, const void* k, const void* 
   p.out_kind = PA_F32;
   p.lse = part_lse;
   p.partial = 1;
-  const LaunchShape ls{D, kv_dtype, q_dtype, RT, NW, MODE_SEGMENT, 0};
+  const LaunchShape ls{D, kv_dtype, q_dtype, RT, NW, MODE_SEGMENT, 0, 0};
   hipError_t e = launch_attention(p, ls, (int64_t)N * Gs * Hkv * RG, stream);
   if (e != hipSuccess) return hip_fail(e, "segment attention launch");
   e = launch_segment_combine(part_o, PA_F32, part_lse, used, bias, N, Gs, Hq, D, out, out_dtype,

@@ -63,6 +63,15 @@ struct TileInfo {
   const char* vp;  // same in V
   int nvalid;      // slots [0, nvalid) hold visible keys (1..16)
   float bias;      // log2-domain logit bias of the tile (fused segments)
+  int key0;        // key index of slot 0 (restricted numbering; paged modes)
+};
+
+// Causal query block (paged): row r of a tile sees keys [lo, hi] of the
+// restricted numbering, hi = L' - sq + t(r), lo = hi - window_left (no lower
+// bound without a window).  `on` is false for tiles every row sees whole.
+struct RowMask {
+  bool on;
+  int hi, lo;
 };
 
 // Copy of a wave-uniform 64-bit value in scalar registers.
@@ -181,10 +190,11 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const void* q, int r
 }
 
 // One 16-key tile against one 16-row tile: S^T, online softmax, O^T += V^T P^T.
-template <int D, int QT>
+template <int D, int QT, bool CAUSAL = false>
 __device__ __forceinline__ void attend_tile(const Frags<D>& f, const u32x4 (&qf)[D / 32],
                                             f32x4 (&acc)[D / 16], float& m_run, float& l_run,
-                                            float scale_log2, float bias, int nvalid, int g4) {
+                                            float scale_log2, float bias, int nvalid, int g4,
+                                            int key0 = 0, RowMask rm = RowMask{false, 0, 0}) {
   f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kc = 0; kc < D / 32; ++kc) sacc = mfma_16x16x32<QT>(f.kf[kc], qf[kc], sacc);
@@ -196,6 +206,15 @@ __device__ __forceinline__ void attend_tile(const Frags<D>& f, const u32x4 (&qf)
     for (int i = 0; i < 4; ++i)
       if (4 * g4 + i >= nvalid) s[i] = kNegInf;
   }
+  if constexpr (CAUSAL) {
+    if (rm.on) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = key0 + 4 * g4 + i;
+        if (key > rm.hi || key < rm.lo) s[i] = kNegInf;
+      }
+    }
+  }
   float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   tmax = max_across_groups(tmax);
   // Lazy rescale: the reference max m_run only moves when some row of the
@@ -204,15 +223,20 @@ __device__ __forceinline__ void attend_tile(const Frags<D>& f, const u32x4 (&qf)
   // Softmax does not depend on the reference, only on it bounding the terms.
   if (__ballot(tmax > m_run + kRescaleSlack) != 0) {
     const float m_new = fmaxf(m_run, tmax);
-    const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile (m_run = -inf)
+    float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile (m_run = -inf)
+    // causal: a row that has seen no key yet (m_new = -inf) keeps its zeros
+    if constexpr (CAUSAL) alpha = m_new == kNegInf ? 1.f : alpha;
     l_run *= alpha;
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) acc[j] *= alpha;
     m_run = m_new;
   }
+  // causal rows with no key so far have only -inf logits: any finite reference
+  float m_ref = m_run;
+  if constexpr (CAUSAL) m_ref = m_run == kNegInf ? 0.f : m_run;
   float pr[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s[i] - m_run);
+  for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s[i] - m_ref);
   l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
   const u32x2 pB = u32x2{pack2<QT>(pr[0], pr[1]), pack2<QT>(pr[2], pr[3])};
 #pragma unroll
@@ -336,8 +360,9 @@ __device__ __forceinline__ int32_t load_phys(const AttnParams& p, const int32_t*
 //   paged:          work item (request, kv head, row group, split)
 //   segment:        (query, segment, kv head, row group)
 //   segment fused:  (query, kv head, row group); segment g's logits get its bias
+// CAUSAL (paged only): bottom-right causal rows with an exact per-token window.
 // ================================================================================
-template <int D, int RT, int NW, int KV, int QT, int MODE>
+template <int D, int RT, int NW, int KV, int QT, int MODE, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   using G = Geo<D, KV>;
   constexpr int KB = G::KB;
@@ -426,6 +451,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
     const int it = wave + NW * k;
     TileInfo ti;
     ti.bias = 0.f;
+    ti.key0 = 0;
     if constexpr (MODE == MODE_PAGED) {
       if (k - k0 >= 64) {
         k0 = k;
@@ -439,6 +465,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
       int page, slot0, nv;
       paged_tile(p, pr, it, page, slot0, nv);
       ti.nvalid = nv;
+      ti.key0 = page * p.P + slot0;
       const int64_t off = ((int64_t)phys * p.page_stride + (int64_t)slot0 * p.token_stride) * KB + head_off_b;
       ti.kp = p.k + off;
       ti.vp = p.v + off;
@@ -495,6 +522,29 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
     for (int j = 0; j < VPL; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // causal bounds of this lane's rows; tiles inside [lo_max, hi_min] need no mask
+  int row_hi[RT] = {}, row_lo[RT] = {};
+  int hi_min = 0, lo_max = 0;
+  if constexpr (CAUSAL) {
+    const int Lr = pr.sv.len;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int t = (row_base + rt * 16 + c16) / p.G;
+      row_hi[rt] = Lr - p.sq + t;
+      row_lo[rt] = p.window_left >= 0 ? row_hi[rt] - p.window_left : INT32_MIN;
+    }
+    hi_min = Lr - p.sq;
+    lo_max = p.window_left >= 0 ? Lr - 1 - p.window_left : INT32_MIN;
+  }
+  auto attend = [&](const Frags<D>& f, const TileInfo& ti) {
+    const bool on = CAUSAL && (ti.key0 + 15 > hi_min || ti.key0 < lo_max);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+      attend_tile<D, QT, CAUSAL>(f, qf[rt], acc[rt], m_run[rt], l_run[rt], p.qk_scale_log2,
+                                 ti.bias, ti.nvalid, g4, ti.key0,
+                                 RowMask{on, row_hi[rt], row_lo[rt]});
+  };
+
   // main loop: tile k+1 is in flight while tile k is computed
   if (wave < n_tiles) {
     TileInfo ti = tile_info(0);
@@ -510,10 +560,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
       }
       Frags<D> f;
       make_frags<D, KV, QT>(cur, f);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        attend_tile<D, QT>(f, qf[rt], acc[rt], m_run[rt], l_run[rt], p.qk_scale_log2, ti.bias,
-                           ti.nvalid, g4);
+      attend(f, ti);
       if (!more) break;
       cur = nxt;
       ti = tn;
@@ -617,7 +664,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
 // that belongs at its position.  Instruction j of a tile is issued by wave
 // j / (IPT / NW).
 // ================================================================================
-template <int D, int NW, int KV, int QT, int NBUF>
+template <int D, int NW, int KV, int QT, int NBUF, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p) {
   using G = Geo<D, KV>;
   constexpr int KB = G::KB;
@@ -792,6 +839,16 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
 #pragma unroll
   for (int j = 0; j < VPL; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // causal bounds of this lane's row; tiles inside [lo_max, hi_min] need no mask
+  int row_hi = 0, row_lo = 0, hi_min = 0, lo_max = 0;
+  if constexpr (CAUSAL) {
+    const int Lr = pr.sv.len;
+    row_hi = Lr - p.sq + (row0 + c16) / p.G;
+    row_lo = p.window_left >= 0 ? row_hi - p.window_left : INT32_MIN;
+    hi_min = Lr - p.sq;
+    lo_max = p.window_left >= 0 ? Lr - 1 - p.window_left : INT32_MIN;
+  }
+
   Cursor ci = cursor_at0();  // next tile to issue
   Cursor cc = cursor_at0();  // next tile to consume
   // prologue: tiles 0 .. NBUF-2 into stages 0 .. NBUF-2
@@ -832,10 +889,13 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
       advance(ci);
     }
     const int nvalid = cursor_valid(cc);
+    const int key0 = cc.tok0;
     advance(cc);
     Frags<D> f;
     read_frags(sc, f);
-    attend_tile<D, QT>(f, qf, acc, m_run, l_run, p.qk_scale_log2, 0.f, nvalid, g4);
+    const bool on = CAUSAL && (key0 + 15 > hi_min || key0 < lo_max);
+    attend_tile<D, QT, CAUSAL>(f, qf, acc, m_run, l_run, p.qk_scale_log2, 0.f, nvalid, g4, key0,
+                               RowMask{on, row_hi, row_lo});
     return true;
   };
   for (int k = 0;; k += NBUF) {
@@ -872,34 +932,38 @@ constexpr int kRingStages = PA_RING_STAGES;  // LDS ring depth of attn_shared_ke
 
 using KernelFn = void (*)(AttnParams);
 
-template <int D, int KV, int QT, int MODE>
+template <int D, int KV, int QT, int MODE, bool C>
 KernelFn pick_keys(int RT, int NW) {
-  if (RT == 1 && NW == 4) return attn_kernel<D, 1, 4, KV, QT, MODE>;
-  if (RT == 1 && NW == 2) return attn_kernel<D, 1, 2, KV, QT, MODE>;
-  if (RT == 1 && NW == 1) return attn_kernel<D, 1, 1, KV, QT, MODE>;
-  if (RT == 2 && NW == 2) return attn_kernel<D, 2, 2, KV, QT, MODE>;
-  if (RT == 4 && NW == 1) return attn_kernel<D, 4, 1, KV, QT, MODE>;
+  if (RT == 1 && NW == 4) return attn_kernel<D, 1, 4, KV, QT, MODE, C>;
+  if (RT == 1 && NW == 2) return attn_kernel<D, 1, 2, KV, QT, MODE, C>;
+  if (RT == 1 && NW == 1) return attn_kernel<D, 1, 1, KV, QT, MODE, C>;
+  if (RT == 2 && NW == 2) return attn_kernel<D, 2, 2, KV, QT, MODE, C>;
+  if (RT == 4 && NW == 1) return attn_kernel<D, 4, 1, KV, QT, MODE, C>;
   return nullptr;
 }
 
-template <int D, int KV, int QT>
+template <int D, int KV, int QT, bool C>
 KernelFn pick_rows(int NW) {
   constexpr int IPT = Geo<D, KV>::IPT;
   if constexpr (IPT % 8 == 0)
-    if (NW == 8) return attn_shared_kernel<D, 8, KV, QT, kRingStages>;
+    if (NW == 8) return attn_shared_kernel<D, 8, KV, QT, kRingStages, C>;
   if constexpr (IPT % 4 == 0)
-    if (NW == 4) return attn_shared_kernel<D, 4, KV, QT, kRingStages>;
-  if (NW == 2) return attn_shared_kernel<D, 2, KV, QT, kRingStages>;
+    if (NW == 4) return attn_shared_kernel<D, 4, KV, QT, kRingStages, C>;
+  if (NW == 2) return attn_shared_kernel<D, 2, KV, QT, kRingStages, C>;
   return nullptr;
 }
 
 template <int D, int KV, int QT, int MODE>
 KernelFn pick_kind(const LaunchShape& s) {
-  if (s.rows_split) {
-    if constexpr (MODE == MODE_PAGED) return pick_rows<D, KV, QT>(s.NW);
-    return nullptr;
+  if constexpr (MODE == MODE_PAGED) {
+    if (s.rows_split)
+      return s.causal ? pick_rows<D, KV, QT, true>(s.NW) : pick_rows<D, KV, QT, false>(s.NW);
+    return s.causal ? pick_keys<D, KV, QT, MODE, true>(s.RT, s.NW)
+                    : pick_keys<D, KV, QT, MODE, false>(s.RT, s.NW);
+  } else {
+    if (s.rows_split || s.causal) return nullptr;
+    return pick_keys<D, KV, QT, MODE, false>(s.RT, s.NW);
   }
-  return pick_keys<D, KV, QT, MODE>(s.RT, s.NW);
 }
 
 template <int D, int MODE>

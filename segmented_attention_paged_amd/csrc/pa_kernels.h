@@ -37,6 +37,7 @@ struct AttnParams {
   const int32_t* used;  // [N, topk+1]
   const float* bias;    // [N, topk]
   int32_t topk, bs, local;
+  int32_t window_left;  // causal: keys >= position - window_left (-1: no lower bound)
 };
 
 // rows_split = 0: attn_kernel (waves split the keys, RT row tiles per wave);
@@ -44,6 +45,7 @@ struct AttnParams {
 // share LDS-staged K/V tiles).
 struct LaunchShape {
   int D, kv_kind, q_kind, RT, NW, mode, rows_split;
+  int causal;  // paged mode: bottom-right causal rows (exact per-token window)
 };
 
 // Rows of attn_kernel's cross-wave merge buffer: a workgroup holds `rows` query

@@ -19,7 +19,7 @@ def gpu_available() -> bool:
     return torch.cuda.is_available()
 
 
-def run_paged(inp, *, num_splits=None, window=None, out_dtype=torch.bfloat16):
+def run_paged(inp, *, num_splits=None, window=None, out_dtype=torch.bfloat16, causal=False):
     import segmented_attention_paged_amd as sap
 
     k, v = sap.kv_halves(inp.cache, inp.D)
@@ -27,7 +27,7 @@ def run_paged(inp, *, num_splits=None, window=None, out_dtype=torch.bfloat16):
         inp.q, k, v, inp.block_table, inp.seq_lens, scale=inp.scale,
         window=inp.window if window is None else window,
         num_splits=inp.num_splits if num_splits is None else num_splits,
-        k_scale=inp.k_scale, v_scale=inp.v_scale, out_dtype=out_dtype)
+        k_scale=inp.k_scale, v_scale=inp.v_scale, out_dtype=out_dtype, causal=causal)
 
 
 def host_subset(inp, requests):
@@ -48,7 +48,7 @@ def host_subset(inp, requests):
     return cache, table, lens.numpy()
 
 
-def oracle_paged(inp, requests=None, kv_heads=None, window=None):
+def oracle_paged(inp, requests=None, kv_heads=None, window=None, causal=False):
     reqs = list(range(inp.B)) if requests is None else list(requests)
     cache, table, lens = host_subset(inp, reqs)
     k, v = kv_halves(to_numpy_bits(cache), inp.D)
@@ -56,7 +56,7 @@ def oracle_paged(inp, requests=None, kv_heads=None, window=None):
     return oracle.paged_attention(
         q, "bf16" if inp.q.dtype == torch.bfloat16 else "fp16", k, v, inp.kv_dtype, table, lens,
         scale=inp.scale, window=inp.window if window is None else window, k_scale=inp.k_scale,
-        v_scale=inp.v_scale, requests=reqs, kv_heads=kv_heads)
+        v_scale=inp.v_scale, requests=reqs, kv_heads=kv_heads, causal=causal)
 
 
 def compare(out, lse, O_ref, L_ref, tol, *, mask=None, what=""):
