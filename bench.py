@@ -101,7 +101,7 @@ def time_events(fn, steps: int, warmup: int, flush=None):
 class PagedBench:
     """Preallocated buffers and closures for one paged workload."""
 
-    def __init__(self, name: str, num_splits=None):
+    def __init__(self, name: str, num_splits=None, causal: bool = False):
         import torch
 
         import segmented_attention_paged_amd as sap
@@ -110,6 +110,7 @@ class PagedBench:
         self.sap = sap
         self.inp = inp = paged_config(name, device="cuda")
         self.name = name
+        self.causal = causal
         self.k, self.v = sap.kv_halves(inp.cache, inp.D)
         self.num_splits = inp.num_splits if num_splits is None else num_splits
         W = inp.block_table.shape[1]
@@ -136,7 +137,8 @@ class PagedBench:
         i = self.inp
         self.sap.paged_attn_run(i.q, self.k, self.v, i.block_table, i.seq_lens, scale=i.scale,
                                 window=i.window, num_splits=self.num_splits, k_scale=i.k_scale,
-                                v_scale=i.v_scale, out=self.out, lse=self.lse, workspace=self.ws)
+                                v_scale=i.v_scale, out=self.out, lse=self.lse, workspace=self.ws,
+                                causal=self.causal)
 
     def kernel(self):
         i = self.inp
@@ -359,6 +361,20 @@ def main(argv=None) -> int:
         log(f"c3_query_block: {ms * 1e3:.1f} us, MFMA {bb.flops / ms / 1e9:.1f} TFLOP/s")
         del bb
         torch.cuda.empty_cache()
+        # the same blocks with the causal mask (exact per-token window for C3w); the
+        # pages read are the same as the dense block's, so the byte count is too
+        causal = {}
+        for name in ("c3_query_block", "c3w_query_block_window"):
+            bb = PagedBench(name, causal=True)
+            ms, _ = time_events(bb.step, max(10, args.steps // 2), max(3, args.warmup // 2))
+            causal[name] = {"us": ms * 1e3, "tokens_per_s": bb.inp.B * bb.inp.sq / (ms / 1e3),
+                            "kv_gbps": bb.kv_bytes / ms / 1e6,
+                            "hbm_frac": bb.kv_bytes / ms / 1e6 / HBM_PEAK_GBPS,
+                            "splits": bb.plan["splits"]}
+            log(f"{name} causal: {ms * 1e3:.1f} us")
+            del bb
+            torch.cuda.empty_cache()
+        result["sq16_block"]["causal"] = causal
 
     if not args.no_kv_write:
         result["kv_write"] = run_kv_write(max(10, args.steps // 2), max(3, args.warmup // 2))
