@@ -135,14 +135,16 @@ class PagedBench:
 
     def step(self):
         i = self.inp
-        self.sap.paged_attn_run(i.q, self.k, self.v, i.block_table, i.seq_lens, scale=i.scale,
+        self.sap.paged_attn_run(i.q, self.k, self.v, i.block_table, i.seq_lens,
+                                scale=i.scale * i.q_scale,
                                 window=i.window, num_splits=self.num_splits, k_scale=i.k_scale,
                                 v_scale=i.v_scale, out=self.out, lse=self.lse, workspace=self.ws,
                                 causal=self.causal)
 
     def kernel(self):
         i = self.inp
-        self.sap.paged_attn_partial(i.q, self.k, self.v, i.block_table, i.seq_lens, scale=i.scale,
+        self.sap.paged_attn_partial(i.q, self.k, self.v, i.block_table, i.seq_lens,
+                                    scale=i.scale * i.q_scale,
                                     num_splits=self.plan["partial_num_splits"], window=i.window,
                                     k_scale=i.k_scale, v_scale=i.v_scale, part_o=self.part_o,
                                     part_lse=self.part_lse)
@@ -375,6 +377,16 @@ def main(argv=None) -> int:
             del bb
             torch.cuda.empty_cache()
         result["sq16_block"]["causal"] = causal
+        # fp8 query against an fp8 cache (q.k on fp8 MFMA, P.V in bf16)
+        bb = PagedBench("c3f_query_block_fp8")
+        ms, _ = time_events(bb.step, max(10, args.steps // 2), max(3, args.warmup // 2))
+        result["sq16_block"]["fp8_query"] = {
+            "workload": "c3f_query_block_fp8", "us": ms * 1e3,
+            "tokens_per_s": bb.inp.B * bb.inp.sq / (ms / 1e3), "kv_gbps": bb.kv_bytes / ms / 1e6,
+            "hbm_frac": bb.kv_bytes / ms / 1e6 / HBM_PEAK_GBPS, "splits": bb.plan["splits"]}
+        log(f"c3f_query_block_fp8: {ms * 1e3:.1f} us, {bb.kv_bytes / ms / 1e6:.0f} GB/s")
+        del bb
+        torch.cuda.empty_cache()
 
     if not args.no_kv_write:
         result["kv_write"] = run_kv_write(max(10, args.steps // 2), max(3, args.warmup // 2))

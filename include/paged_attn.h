@@ -79,9 +79,14 @@ typedef struct pa_kv_desc {
 /* Paged attention of a uniform query block: work partition, window restriction,
  * block-table gather, attention, and the split combine when splits > 1.
  *
- * q           [B, query_len, Hq, D] contiguous, q_dtype PA_BF16 | PA_FP16.
- *             A 16-bit cache must have the query's dtype; an fp8 cache takes
- *             either 16-bit query (it is decoded exactly to that type).
+ * q           [B, query_len, Hq, D] contiguous, q_dtype PA_BF16 | PA_FP16 |
+ *             PA_FP8_E4M3.  A 16-bit cache must have the query's dtype; an
+ *             fp8 cache takes either 16-bit query (K and V are decoded exactly
+ *             to that type) or an fp8 query (flashinfer_ts keeps q and K/V
+ *             dtypes matched; the query arrives quantized): q.k then runs on
+ *             fp8 MFMA and P.V in bf16.  An fp8 query's own scale is folded
+ *             into `scale` by the caller (the page's bmm1_scale = scale *
+ *             q_scale * k_scale).
  * block_table [B, bt_width] int32 with row stride bt_row_stride (elements);
  *             column j of row b names the pool page holding tokens
  *             [j*P, (j+1)*P) of request b.  Columns >= ceil(L_b / P) are

@@ -94,6 +94,7 @@ def paged_attention(
     kv_heads=None,
     token_range=None,
     causal: bool = False,
+    q_scale: float = 1.0,
 ):
     """Attention of a uniform query block over a paged cache.
 
@@ -112,8 +113,12 @@ def paged_attention(
     the block's tokens sit at positions L - sq + t, token t sees keys
     j <= L - sq + t and, with a window, j >= L - sq + t - (window - 1): an
     exact per-token window of ``window`` keys ending at the token itself.
+
+    q_scale: the real query is q_scale times the stored one (an fp8 query
+    arrives quantized; flashinfer_ts ``forward`` folds its scale into
+    bmm1_scale together with k_scale).
     """
-    qv = decode(q, q_dtype)
+    qv = decode(q, q_dtype) * q_scale
     B, sq, Hq, D = qv.shape
     pool, Hkv, P, Dk = k_pages.shape
     if Dk != D or Hq % Hkv:

@@ -102,7 +102,8 @@ def paged_attn_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_tabl
         raise TypeError("block_table and seq_lens must be int32")
     desc = kv_desc(k, v, k_scale=k_scale, v_scale=v_scale)
     if out is None:
-        out = torch.empty((B, sq, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+        default = q.dtype if q.dtype in (torch.bfloat16, torch.float16) else torch.bfloat16
+        out = torch.empty((B, sq, Hq, D), dtype=out_dtype or default, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, sq, Hq), dtype=torch.float32, device=q.device)
     W = block_table.shape[1]

@@ -115,12 +115,14 @@ int check_paged(const void* q, int32_t q_dtype, const pa_kv_desc* kv, const int3
                 int32_t query_len, int32_t Hq, int32_t D, float scale) {
   if (B < 0 || query_len < 0) return fail(PA_EINVAL, "B and query_len must be >= 0");
   if (!kv) return fail(PA_EINVAL, "kv descriptor is NULL");
-  if (q_dtype != PA_BF16 && q_dtype != PA_FP16)
-    return fail(PA_ENOTSUP, "query dtype must be bf16 or fp16 (got %d)", q_dtype);
+  if (q_dtype != PA_BF16 && q_dtype != PA_FP16 && q_dtype != PA_FP8_E4M3)
+    return fail(PA_ENOTSUP, "query dtype must be bf16, fp16 or fp8_e4m3 (got %d)", q_dtype);
   if (kv->dtype != PA_BF16 && kv->dtype != PA_FP16 && kv->dtype != PA_FP8_E4M3)
     return fail(PA_ENOTSUP, "kv dtype must be bf16, fp16 or fp8_e4m3 (got %d)", kv->dtype);
   if (kv->dtype != PA_FP8_E4M3 && kv->dtype != q_dtype)
     return fail(PA_ENOTSUP, "a 16-bit cache needs a query of the same dtype");
+  if (q_dtype == PA_FP8_E4M3 && kv->dtype != PA_FP8_E4M3)
+    return fail(PA_ENOTSUP, "an fp8 query needs an fp8 cache");
   if (D != 64 && D != 128) return fail(PA_EINVAL, "head_dim must be 64 or 128 (got %d)", D);
   if (Hq <= 0 || kv->num_kv_heads <= 0 || Hq % kv->num_kv_heads)
     return fail(PA_EINVAL, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, kv->num_kv_heads);

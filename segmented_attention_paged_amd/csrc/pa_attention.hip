@@ -122,17 +122,27 @@ struct Raw {
   uint32_t v[4][Geo<D, KV>::VDW];
 };
 
-// MFMA operands of one tile in the query's 16-bit type.
-template <int D>
+// MFMA operands of one tile: K in the query's S^T operand type, V^T in the
+// P.V type (the query's 16-bit type; bf16 for an fp8 query).
+template <int D, int QT>
 struct Frags {
-  u32x4 kf[D / 32];
+  typename QTypes<QT>::QOp kf[D / 32];
   u32x2 vA[D / 16];
 };
 
 template <int D, int KV, int QT>
-__device__ __forceinline__ void make_frags(const Raw<D, KV>& r, Frags<D>& f) {
+__device__ __forceinline__ void make_frags(const Raw<D, KV>& r, Frags<D, QT>& f) {
   using G = Geo<D, KV>;
-  if constexpr (KV == K_FP8) {
+  constexpr int PV = QTypes<QT>::PV;
+  if constexpr (QT == K_FP8) {
+    static_assert(KV == K_FP8, "an fp8 query needs an fp8 cache");
+    // raw bytes are the fp8 operand: piece i = head-dim bytes 64i + 16*(l/16) .. +15
+#pragma unroll
+    for (int c2 = 0; c2 < G::KLD; ++c2) {
+      f.kf[2 * c2] = u32x2{r.k[c2][0], r.k[c2][1]};
+      f.kf[2 * c2 + 1] = u32x2{r.k[c2][2], r.k[c2][3]};
+    }
+  } else if constexpr (KV == K_FP8) {
 #pragma unroll
     for (int c2 = 0; c2 < G::KLD; ++c2) {
       uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
@@ -152,7 +162,7 @@ __device__ __forceinline__ void make_frags(const Raw<D, KV>& r, Frags<D>& f) {
   for (int i = 0; i < 4; ++i) {
     if constexpr (KV == K_FP8) {
 #pragma unroll
-      for (int w = 0; w < G::VDW; ++w) fp8x4_to_16<QT>(r.v[i][w], v16[i][2 * w], v16[i][2 * w + 1]);
+      for (int w = 0; w < G::VDW; ++w) fp8x4_to_16<PV>(r.v[i][w], v16[i][2 * w], v16[i][2 * w + 1]);
     } else {
 #pragma unroll
       for (int w = 0; w < G::VDW; ++w) v16[i][w] = r.v[i][w];
@@ -168,36 +178,40 @@ __device__ __forceinline__ void make_frags(const Raw<D, KV>& r, Frags<D>& f) {
   }
 }
 
-// Query fragments (B operand of S^T = K Q^T) for row tile starting at `row0`.
-template <int D, int KV>
-__device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const void* q, int row0, int R, int G,
-                                       int kvh, int qb, int sq, int Hq, int g4, int c16) {
+// Query fragments (B operand of S^T = K Q^T) for row tile starting at `row0`:
+// the same head dims per lane and register as the K operand of make_frags.
+template <int D, int KV, int QT>
+__device__ __forceinline__ void load_q(typename QTypes<QT>::QOp (&qf)[D / 32], const void* q,
+                                       int row0, int R, int G, int kvh, int qb, int sq, int Hq,
+                                       int g4, int c16) {
+  using QOp = typename QTypes<QT>::QOp;
+  constexpr int EB = QT == K_FP8 ? 1 : 2;
   const int rr = row0 + c16;
   if (rr < R) {
     const int t = rr / G, gg = rr % G;
     const int h = kvh * G + gg;
-    const uint16_t* qrow =
-        reinterpret_cast<const uint16_t*>(q) + (((int64_t)qb * sq + t) * Hq + h) * D;
+    const char* qrow = static_cast<const char*>(q) + ((((int64_t)qb * sq + t) * Hq + h) * D) * EB;
 #pragma unroll
     for (int kc = 0; kc < D / 32; ++kc) {
       const int d = (KV == K_FP8) ? 64 * (kc >> 1) + 16 * g4 + 8 * (kc & 1) : 32 * kc + 8 * g4;
-      qf[kc] = *reinterpret_cast<const u32x4*>(qrow + d);
+      qf[kc] = *reinterpret_cast<const QOp*>(qrow + d * EB);
     }
   } else {
 #pragma unroll
-    for (int kc = 0; kc < D / 32; ++kc) qf[kc] = u32x4{0u, 0u, 0u, 0u};
+    for (int kc = 0; kc < D / 32; ++kc) qf[kc] = QOp{};
   }
 }
 
 // One 16-key tile against one 16-row tile: S^T, online softmax, O^T += V^T P^T.
 template <int D, int QT, bool CAUSAL = false>
-__device__ __forceinline__ void attend_tile(const Frags<D>& f, const u32x4 (&qf)[D / 32],
+__device__ __forceinline__ void attend_tile(const Frags<D, QT>& f,
+                                            const typename QTypes<QT>::QOp (&qf)[D / 32],
                                             f32x4 (&acc)[D / 16], float& m_run, float& l_run,
                                             float scale_log2, float bias, int nvalid, int g4,
                                             int key0 = 0, RowMask rm = RowMask{false, 0, 0}) {
   f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kc = 0; kc < D / 32; ++kc) sacc = mfma_16x16x32<QT>(f.kf[kc], qf[kc], sacc);
+  for (int kc = 0; kc < D / 32; ++kc) sacc = qk_mfma<QT>(f.kf[kc], qf[kc], sacc);
   float s[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) s[i] = sacc[i] * scale_log2 + bias;
@@ -238,9 +252,10 @@ __device__ __forceinline__ void attend_tile(const Frags<D>& f, const u32x4 (&qf)
 #pragma unroll
   for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s[i] - m_ref);
   l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-  const u32x2 pB = u32x2{pack2<QT>(pr[0], pr[1]), pack2<QT>(pr[2], pr[3])};
+  constexpr int PV = QTypes<QT>::PV;
+  const u32x2 pB = u32x2{pack2<PV>(pr[0], pr[1]), pack2<PV>(pr[2], pr[3])};
 #pragma unroll
-  for (int j = 0; j < D / 16; ++j) acc[j] = mfma_16x16x16<QT>(f.vA[j], pB, acc[j]);
+  for (int j = 0; j < D / 16; ++j) acc[j] = mfma_16x16x16<PV>(f.vA[j], pB, acc[j]);
 }
 
 // Write one lane's part of a finished 16-row tile: row row0 + l%16, values
@@ -436,10 +451,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   }
 
   const int row_base = rg * ROWS;
-  u32x4 qf[RT][D / 32];
+  typename QTypes<QT>::QOp qf[RT][D / 32];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
-    load_q<D, KV>(qf[rt], p.q, row_base + rt * 16, p.R, p.G, kvh, qb, p.sq, p.Hq, g4, c16);
+    load_q<D, KV, QT>(qf[rt], p.q, row_base + rt * 16, p.R, p.G, kvh, qb, p.sq, p.Hq, g4, c16);
 
   // paged: lane i caches the pool page of the wave's tile k0 + i
   int32_t phys_vec = 0;
@@ -536,7 +551,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
     hi_min = Lr - p.sq;
     lo_max = p.window_left >= 0 ? Lr - 1 - p.window_left : INT32_MIN;
   }
-  auto attend = [&](const Frags<D>& f, const TileInfo& ti) {
+  auto attend = [&](const Frags<D, QT>& f, const TileInfo& ti) {
     const bool on = CAUSAL && (ti.key0 + 15 > hi_min || ti.key0 < lo_max);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -558,7 +573,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
         tn = tile_info(k + 1);
         load_tile(nxt, tn);
       }
-      Frags<D> f;
+      Frags<D, QT> f;
       make_frags<D, KV, QT>(cur, f);
       attend(f, ti);
       if (!more) break;
@@ -707,8 +722,8 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
   const int n_tiles = pr.n_tiles;
   const int row0 = rg * (NW * 16) + wave * 16;
 
-  u32x4 qf[D / 32];
-  load_q<D, KV>(qf, p.q, row0, p.R, p.G, kvh, item, p.sq, p.Hq, g4, c16);
+  typename QTypes<QT>::QOp qf[D / 32];
+  load_q<D, KV, QT>(qf, p.q, row0, p.R, p.G, kvh, item, p.sq, p.Hq, g4, c16);
 
   // Pool pages, 64 tiles at a time: lane i of phys_vec holds the page of tile
   // k0 + i.  Lanes past the last tile read a valid (clamped) column that is
@@ -815,7 +830,7 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
       v_lds[i] = 16 * (t * G::CPK + (cv ^ (t & G::SWZ))) + (vbyte & 15);
     }
   }
-  auto read_frags = [&](auto sc, Frags<D>& f) {
+  auto read_frags = [&](auto sc, Frags<D, QT>& f) {
     const char* st = stage_buf(sc);
     if constexpr (TR) {
 #pragma unroll
@@ -891,7 +906,7 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
     const int nvalid = cursor_valid(cc);
     const int key0 = cc.tok0;
     advance(cc);
-    Frags<D> f;
+    Frags<D, QT> f;
     read_frags(sc, f);
     const bool on = CAUSAL && (key0 + 15 > hi_min || key0 < lo_max);
     attend_tile<D, QT, CAUSAL>(f, qf, acc, m_run, l_run, p.qk_scale_log2, 0.f, nvalid, g4, key0,
@@ -973,6 +988,7 @@ KernelFn pick_types(const LaunchShape& s) {
   if constexpr (MODE == MODE_PAGED) {
     if (s.kv_kind == K_FP8 && s.q_kind == K_BF16) return pick_kind<D, K_FP8, K_BF16, MODE>(s);
     if (s.kv_kind == K_FP8 && s.q_kind == K_FP16) return pick_kind<D, K_FP8, K_FP16, MODE>(s);
+    if (s.kv_kind == K_FP8 && s.q_kind == K_FP8) return pick_kind<D, K_FP8, K_FP8, MODE>(s);
   }
   return nullptr;
 }

@@ -40,6 +40,32 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(const u32x4& a, const u32x4& b, f
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8>(a), bitcast<f16x8>(b), c, 0, 0, 0);
 }
 
+// Operand types of a query kind: the S^T operands (K and Q^T, 32 head-dim
+// values per lane group) and the element type of P and V in O^T += V^T P^T.
+// A 16-bit query runs both products in its own type; an fp8 query runs S^T
+// on fp8 MFMA (the cache is fp8 too) and O^T in bf16.
+template <int QT>
+struct QTypes {
+  using QOp = u32x4;  // 8 16-bit values
+  static constexpr int PV = QT;
+};
+template <>
+struct QTypes<K_FP8> {
+  using QOp = u32x2;  // 8 e4m3fn bytes
+  static constexpr int PV = K_BF16;
+};
+
+// S^T tile for a query kind (the mfma_16x16x32 layout above for every kind;
+// gfx950's fp8 MFMA takes OCP e4m3fn, checked on the GPU by a probe).
+template <int QT>
+__device__ __forceinline__ f32x4 qk_mfma(const typename QTypes<QT>::QOp& a,
+                                         const typename QTypes<QT>::QOp& b, f32x4 c) {
+  if constexpr (QT == K_FP8)
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(bitcast<long>(a), bitcast<long>(b), c, 0, 0, 0);
+  else
+    return mfma_16x16x32<QT>(a, b, c);
+}
+
 // O^T tile: 16 head-dim values x 16 rows, contraction over 16 keys.
 // A = V^T (lane l: dim-row l%16, keys 4*(l/16)+i), B = P^T (lane l: keys
 // 4*(l/16)+i, row l%16) -- exactly the C layout of mfma_16x16x32 above.

@@ -24,7 +24,7 @@ def run_paged(inp, *, num_splits=None, window=None, out_dtype=torch.bfloat16, ca
 
     k, v = sap.kv_halves(inp.cache, inp.D)
     return sap.paged_attn_run(
-        inp.q, k, v, inp.block_table, inp.seq_lens, scale=inp.scale,
+        inp.q, k, v, inp.block_table, inp.seq_lens, scale=inp.scale * inp.q_scale,
         window=inp.window if window is None else window,
         num_splits=inp.num_splits if num_splits is None else num_splits,
         k_scale=inp.k_scale, v_scale=inp.v_scale, out_dtype=out_dtype, causal=causal)
@@ -53,8 +53,9 @@ def oracle_paged(inp, requests=None, kv_heads=None, window=None, causal=False):
     cache, table, lens = host_subset(inp, reqs)
     k, v = kv_halves(to_numpy_bits(cache), inp.D)
     q = to_numpy_bits(inp.q.cpu())
+    q_dtype = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.uint8: "fp8_e4m3"}[inp.q.dtype]
     return oracle.paged_attention(
-        q, "bf16" if inp.q.dtype == torch.bfloat16 else "fp16", k, v, inp.kv_dtype, table, lens,
+        q, q_dtype, k, v, inp.kv_dtype, table, lens, q_scale=inp.q_scale,
         scale=inp.scale, window=inp.window if window is None else window, k_scale=inp.k_scale,
         v_scale=inp.v_scale, requests=reqs, kv_heads=kv_heads, causal=causal)
 

@@ -125,6 +125,21 @@ def test_matches_torch_sdpa_fp64():
         np.testing.assert_allclose(LSE[b], lse, rtol=0, atol=1e-12)
 
 
+def test_fp8_query_scale_folding_equals_prescaled_query():
+    inp = make_paged(B=2, sq=3, Hq=4, Hkv=2, D=16, P=4, seq_lens=[5, 11], seed=23,
+                     kv_dtype="fp8_e4m3", q_dtype="fp8_e4m3")
+    q8 = to_numpy_bits(inp.q)
+    k, v = kv_halves(to_numpy_bits(inp.cache), inp.D)
+    bt, lens = inp.block_table.numpy(), inp.seq_lens.numpy()
+    kw = dict(scale=inp.scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
+    O, L = oracle.paged_attention(q8, "fp8_e4m3", k, v, "fp8_e4m3", bt, lens, q_scale=inp.q_scale, **kw)
+    qf = oracle.e4m3fn_to_f64(q8) * inp.q_scale
+    O2, L2 = oracle.paged_attention(qf, "f64", k, v, "fp8_e4m3", bt, lens, **kw)
+    np.testing.assert_allclose(O, O2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, L2, rtol=0, atol=1e-12)
+    assert inp.q.dtype == torch.uint8 and 0.5 <= inp.q_scale <= 2.0
+
+
 # Causal mask with an exact per-token window --------------------------------
 @pytest.mark.parametrize("window", [0, 1, 3, 9])
 def test_causal_brute_force_loops_agree(window):

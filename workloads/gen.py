@@ -58,6 +58,8 @@ class PagedInputs:
     block_table: torch.Tensor  # [B, W] int32
     seq_lens: torch.Tensor  # [B] int32 (includes the query block)
     poison: bool
+    q_dtype: str = "bf16"  # or "fp8_e4m3": q holds e4m3fn bytes, real q = q_scale * q
+    q_scale: float = 1.0
 
     def to(self, device) -> "PagedInputs":
         return replace(
@@ -164,6 +166,7 @@ def make_paged(
     table_width: int = 0,
     name: str = "paged",
     device=None,
+    q_dtype: str = "bf16",
 ) -> PagedInputs:
     """Draw one paged-attention workload.
 
@@ -175,6 +178,8 @@ def make_paged(
     """
     if kv_dtype not in ("bf16", "fp8_e4m3"):
         raise ValueError(kv_dtype)
+    if q_dtype not in ("bf16", "fp8_e4m3") or (q_dtype == "fp8_e4m3" and kv_dtype != "fp8_e4m3"):
+        raise ValueError(q_dtype)
     g = torch.Generator().manual_seed(int(seed))
 
     # 1. sequence lengths
@@ -209,7 +214,7 @@ def make_paged(
     gd = g
     if device is not None and torch.device(device).type != "cpu":
         gd = torch.Generator(device=device).manual_seed(int(seed) + DEVICE_SEED_OFFSET)
-    q = _randn_bf16((B, sq, Hq, D), gd)
+    q = _randn_bf16((B, sq, Hq, D), gd) if q_dtype == "bf16" else _randn_e4m3_bytes((B, sq, Hq, D), gd)
     if kv_dtype == "bf16":
         cache = _randn_bf16((pool, Hkv, P, 2 * D), gd)
     else:
@@ -221,6 +226,9 @@ def make_paged(
         k_scale, v_scale = float(sc[0]), float(sc[1])
     else:
         k_scale = v_scale = 1.0
+    # 6. fp8 query scale (real q = q_scale * stored q)
+    q_scale = float(torch.rand((), generator=g, dtype=torch.float64) * 1.5 + 0.5) \
+        if q_dtype == "fp8_e4m3" else 1.0
 
     if poison:
         fill_value = float("nan") if kv_dtype == "bf16" else NAN_E4M3_BYTE
@@ -255,6 +263,8 @@ def make_paged(
         block_table=table,
         seq_lens=lens.to(torch.int32),
         poison=poison,
+        q_dtype=q_dtype,
+        q_scale=q_scale,
     )
 
 
@@ -345,6 +355,10 @@ CONFIGS = {
     "c3w_query_block_window": dict(
         kind="paged", B=32, sq=16, Hq=32, Hkv=8, D=128, P=16, seq_lens=("uniform", 1024, 32768),
         table_width=2048, window=4096, seed=1003,
+    ),
+    "c3f_query_block_fp8": dict(
+        kind="paged", B=32, sq=16, Hq=32, Hkv=8, D=128, P=16, seq_lens=("uniform", 1024, 32768),
+        table_width=2048, kv_dtype="fp8_e4m3", q_dtype="fp8_e4m3", seed=1003,
     ),
     "c4_split_kv": dict(
         kind="paged", B=8, sq=1, Hq=64, Hkv=8, D=128, P=16, seq_lens=[131072] * 8,
