@@ -130,33 +130,41 @@ struct Frags {
   u32x2 vA[D / 16];
 };
 
+// S^T operand K from the raw K pieces of one lane (key l%16; piece i holds
+// stored bytes 64i + 16*(l/16) .. +15 of the key row).
 template <int D, int KV, int QT>
-__device__ __forceinline__ void make_frags(const Raw<D, KV>& r, Frags<D, QT>& f) {
+__device__ __forceinline__ void k_operands(const u32x4 (&rk)[Geo<D, KV>::KLD], Frags<D, QT>& f) {
   using G = Geo<D, KV>;
-  constexpr int PV = QTypes<QT>::PV;
   if constexpr (QT == K_FP8) {
     static_assert(KV == K_FP8, "an fp8 query needs an fp8 cache");
-    // raw bytes are the fp8 operand: piece i = head-dim bytes 64i + 16*(l/16) .. +15
+    // the stored bytes are the fp8 operand
 #pragma unroll
     for (int c2 = 0; c2 < G::KLD; ++c2) {
-      f.kf[2 * c2] = u32x2{r.k[c2][0], r.k[c2][1]};
-      f.kf[2 * c2 + 1] = u32x2{r.k[c2][2], r.k[c2][3]};
+      f.kf[2 * c2] = u32x2{rk[c2][0], rk[c2][1]};
+      f.kf[2 * c2 + 1] = u32x2{rk[c2][2], rk[c2][3]};
     }
   } else if constexpr (KV == K_FP8) {
 #pragma unroll
     for (int c2 = 0; c2 < G::KLD; ++c2) {
       uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
-      fp8x4_to_16<QT>(r.k[c2][0], a0, a1);
-      fp8x4_to_16<QT>(r.k[c2][1], a2, a3);
-      fp8x4_to_16<QT>(r.k[c2][2], b0, b1);
-      fp8x4_to_16<QT>(r.k[c2][3], b2, b3);
+      fp8x4_to_16<QT>(rk[c2][0], a0, a1);
+      fp8x4_to_16<QT>(rk[c2][1], a2, a3);
+      fp8x4_to_16<QT>(rk[c2][2], b0, b1);
+      fp8x4_to_16<QT>(rk[c2][3], b2, b3);
       f.kf[2 * c2] = u32x4{a0, a1, a2, a3};
       f.kf[2 * c2 + 1] = u32x4{b0, b1, b2, b3};
     }
   } else {
 #pragma unroll
-    for (int kc = 0; kc < G::NKC; ++kc) f.kf[kc] = r.k[kc];
+    for (int kc = 0; kc < G::NKC; ++kc) f.kf[kc] = rk[kc];
   }
+}
+
+template <int D, int KV, int QT>
+__device__ __forceinline__ void make_frags(const Raw<D, KV>& r, Frags<D, QT>& f) {
+  using G = Geo<D, KV>;
+  constexpr int PV = QTypes<QT>::PV;
+  k_operands<D, KV, QT>(r.k, f);
   uint32_t v16[4][G::VPL / 2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -804,10 +812,16 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
   //  r/4 + 4e, e = 0..3 of its group.  So the lane with a = l%4,
   //  e = (l%16)/4 addresses dims 16j + 4a .. +3 of key 4*(l/16) + e, and lane
   //  l receives dim 16j + l%16 of keys 4*(l/16) + e: the A operand of V^T.
-  //  fp8 K/V: V rows are read as stored and transposed in registers (the
-  //  interleaved layout), after the fp8 -> 16-bit conversion.
+  //  fp8 K/V: 8-bit transposing reads (ds_read_b64_tr_b8), then an exact
+  //  fp8 -> 16-bit decode; same blocked layout.  Within each 16-lane group,
+  //  lane 8a+b of such a read receives byte b of the 8-byte pieces addressed
+  //  by lanes 2e+a, e = 0..7 of its group.  Read p serves PV MFMAs 2p and
+  //  2p+1: the lane with e = (l%16)/2, a = l%2 addresses key 4*(l/16) + e%4,
+  //  head dims 16*(2p + e/4) + 8a .. +7, so lane l receives dim 16*(2p) + l%16
+  //  of keys 4*(l/16) + 0..3 in bytes 0..3 and dim 16*(2p+1) + l%16 of the
+  //  same keys in bytes 4..7.
   constexpr bool TR = KV != K_FP8;
-  constexpr int NVL = TR ? VPL : 4;
+  constexpr int NVL = TR ? VPL : VPL / 2;
   int k_lds[G::KLD], v_lds[NVL];
 #pragma unroll
   for (int i = 0; i < G::KLD; ++i) {
@@ -822,12 +836,12 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
       v_lds[j] = 16 * (t * G::CPK + (cv ^ (t & G::SWZ))) + 8 * (a & 1);
     }
   } else {
-    const int vbyte = G::VB * c16;  // byte offset of this lane's values inside a V row
-    const int cv = G::CPK / 2 + (vbyte >> 4);
+    const int e = c16 >> 1, a = c16 & 1;
+    const int t = 4 * g4 + (e & 3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 4 * g4 + i;
-      v_lds[i] = 16 * (t * G::CPK + (cv ^ (t & G::SWZ))) + (vbyte & 15);
+    for (int pp = 0; pp < VPL / 2; ++pp) {
+      const int cv = G::CPK / 2 + 2 * pp + (e >> 2);  // 16 bytes of V per PV MFMA
+      v_lds[pp] = 16 * (t * G::CPK + (cv ^ (t & G::SWZ))) + 8 * a;
     }
   }
   auto read_frags = [&](auto sc, Frags<D, QT>& f) {
@@ -840,12 +854,21 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
         f.vA[j] = bitcast<u32x2>(__builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(st + v_lds[j])));
     } else {
-      Raw<D, KV> r;
+      u32x4 rk[G::KLD];
 #pragma unroll
-      for (int i = 0; i < G::KLD; ++i) r.k[i] = *reinterpret_cast<const u32x4*>(st + k_lds[i]);
+      for (int i = 0; i < G::KLD; ++i) rk[i] = *reinterpret_cast<const u32x4*>(st + k_lds[i]);
+      k_operands<D, KV, QT>(rk, f);
+      constexpr int PV = QTypes<QT>::PV;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lds_read_v<G::VDW>(r.v[i], st + v_lds[i]);
-      make_frags<D, KV, QT>(r, f);
+      for (int pp = 0; pp < VPL / 2; ++pp) {
+        const auto x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i32*)(st + v_lds[pp]));
+        uint32_t lo, hi;
+        fp8x4_to_16<PV>((uint32_t)x[0], lo, hi);
+        f.vA[2 * pp] = u32x2{lo, hi};
+        fp8x4_to_16<PV>((uint32_t)x[1], lo, hi);
+        f.vA[2 * pp + 1] = u32x2{lo, hi};
+      }
     }
   };
 
@@ -933,7 +956,7 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
   if (rr < p.R) {
     const int t = rr / p.G, gg = rr % p.G;
     const int64_t orow = ((int64_t)item * p.sq + t) * p.Hq + kvh * p.G + gg;
-    store_tile<D, TR>(acc, m_run, l_run, p.v_scale, o_base, p.out_kind, lse_base, orow, p.partial, g4);
+    store_tile<D, true>(acc, m_run, l_run, p.v_scale, o_base, p.out_kind, lse_base, orow, p.partial, g4);
   }
 }
 

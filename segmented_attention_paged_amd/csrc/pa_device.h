@@ -16,6 +16,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
 
 // Element kinds (numerically equal to the public pa_dtype codes).
 enum Kind : int { K_BF16 = 1, K_FP16 = 2, K_FP8 = 3, K_F32 = 4 };
