@@ -349,6 +349,18 @@ __device__ __forceinline__ void wait_tiles_ahead(int ahead) {
   }
 }
 
+// f(integral_constant<S>) for S = B .. E-1 in order while it returns true
+// (compile-time stage numbers for the unrolled ring loop).
+template <int B, int E, typename F>
+__device__ __forceinline__ bool static_all(F&& f) {
+  if constexpr (B < E) {
+    if (!f(std::integral_constant<int, B>{})) return false;
+    return static_all<B + 1, E>(f);
+  } else {
+    return true;
+  }
+}
+
 // Longest-first dispatch: the request with the given rank when requests are
 // ordered by decreasing visible length (ties by index).  Work items are laid
 // out rank-major, so the hardware starts the longest requests' workgroups
@@ -694,7 +706,7 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
   constexpr int VPL = G::VPL;
   constexpr int IPW = G::IPT / NW;  // direct-to-LDS loads per wave per tile
   static_assert(G::IPT % NW == 0 && IPW >= 1, "tile loads must split evenly over the waves");
-  static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
+  static_assert(NBUF >= 2 && NBUF <= 8, "ring depth");
   // One LDS object per ring stage, addressed with compile-time stage numbers
   // (the tile loop is unrolled NBUF times).  The compiler can then tell that
   // reading stage s does not depend on the direct-to-LDS loads still landing
@@ -703,12 +715,20 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
   __shared__ __attribute__((aligned(1024))) char ring1[G::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char ring2[NBUF > 2 ? G::TILE_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) char ring3[NBUF > 3 ? G::TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char ring4[NBUF > 4 ? G::TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char ring5[NBUF > 5 ? G::TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char ring6[NBUF > 6 ? G::TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char ring7[NBUF > 7 ? G::TILE_BYTES : 16];
   auto stage_buf = [&](auto sc) -> char* {
     constexpr int s = decltype(sc)::value;
     if constexpr (s == 0) return ring0;
     else if constexpr (s == 1) return ring1;
     else if constexpr (s == 2) return ring2;
-    else return ring3;
+    else if constexpr (s == 3) return ring3;
+    else if constexpr (s == 4) return ring4;
+    else if constexpr (s == 5) return ring5;
+    else if constexpr (s == 6) return ring6;
+    else return ring7;
   };
 
   const int lane = threadIdx.x & 63;
@@ -899,9 +919,10 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
       }
     }
   };
-  prologue(std::integral_constant<int, 0>{});
-  prologue(std::integral_constant<int, 1>{});
-  prologue(std::integral_constant<int, 2>{});
+  static_all<0, NBUF - 1>([&](auto sc) {
+    prologue(sc);
+    return true;
+  });
   // Settle the query fragments (and the first table batch) here, behind the
   // prologue's loads.  Left to the first use inside the tile loop, the wait
   // would stay in the loop and, merged with the ring loads of the previous
@@ -936,14 +957,8 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
                                RowMask{on, row_hi, row_lo});
     return true;
   };
-  for (int k = 0;; k += NBUF) {
-    if (!step(std::integral_constant<int, 0>{}, k)) break;
-    if (!step(std::integral_constant<int, 1>{}, k + 1)) break;
-    if constexpr (NBUF > 2)
-      if (!step(std::integral_constant<int, 2 % NBUF>{}, k + 2)) break;
-    if constexpr (NBUF > 3)
-      if (!step(std::integral_constant<int, 3 % NBUF>{}, k + 3)) break;
-  }
+  for (int k = 0;; k += NBUF)
+    if (!static_all<0, NBUF>([&](auto sc) { return step(sc, k + decltype(sc)::value); })) break;
 
   l_run = sum_across_groups(l_run);
   float* lse_base = p.lse;
