@@ -93,6 +93,31 @@ def test_special_values_quantise_like_the_oracle(sap):
     np.testing.assert_array_equal(gv, vc)
 
 
+def test_quotient_ties_after_fp32_rounding(sap):
+    # values whose exact quotient x / s sits a hair above an e4m3fn midpoint but
+    # rounds onto it in fp32: the tie must go to the even code, as in the oracle
+    cases = []
+    for s in np.arange(1.01, 2.0, 0.001, dtype=np.float64).astype(np.float32):
+        for mid in (1.0625, 2.375, 0.15625, 13.0):
+            x = np.float32(mid * float(s))
+            if float(x) / float(s) != mid and np.float32(x) / np.float32(s) == np.float32(mid):
+                cases.append((float(s), x))
+    # the cache write takes bf16/fp16 rows: keep the cases whose x is an fp16 value
+    cases = [(s, x) for s, x in cases if np.float32(np.float16(x)) == x][:8]
+    assert cases
+    for sc, x in cases:
+        w = make_kv_write(T=4, Hkv=1, D=64, P=16, pages=1, seed=2, in_dtype="fp16",
+                          cache_dtype="fp8_e4m3")
+        w.k_scale = w.v_scale = sc
+        w.key = torch.full((w.T, 1, w.D), float(x), dtype=torch.float16)
+        w.value = torch.full((w.T, 1, w.D), -float(x), dtype=torch.float16)
+        cache, _, _ = _gpu_write(sap, w)
+        kc, vc = _oracle_write(w)
+        gk, gv = np_halves(to_numpy_bits(cache.cpu()), w.D)
+        np.testing.assert_array_equal(gk, kc)
+        np.testing.assert_array_equal(gv, vc)
+
+
 def test_separate_planes_and_token_strides(sap):
     # K and V in separate compact planes; key/value rows taken from a wider
     # fused buffer (token stride larger than Hkv*D)

@@ -50,6 +50,19 @@ def test_encoder_ties_go_to_the_even_code():
     assert oracle.e4m3fn_encode(x).tolist() == [0x38, 0x3A, 0x00, 0x02, 0x02, 0xB8]
 
 
+def test_quantize_rounds_the_quotient_to_fp32_first():
+    # x / s lands a hair above the midpoint 1.0625 of 0x38 / 0x39 in exact
+    # arithmetic but on it after rounding to fp32, where the tie goes to the
+    # even code 0x38 (an fp64 quotient would give 0x39)
+    found = 0
+    for s in np.arange(1.01, 2.0, 0.001, dtype=np.float64).astype(np.float32):
+        x = np.float32(1.0625 * float(s))
+        if float(x) / float(s) > 1.0625 and np.float32(x) / np.float32(s) == np.float32(1.0625):
+            assert oracle.quantize_e4m3fn(np.array([x]), float(s)).tolist() == [0x38]
+            found += 1
+    assert found > 10
+
+
 def test_quantize_divides_in_fp32():
     # 1/3 is rounded to fp32 before encoding: (x / 3) for x = 3 * code value is exact
     vals = oracle.E4M3FN_TABLE[0x20:0x60].astype(np.float32) * np.float32(3.0)
