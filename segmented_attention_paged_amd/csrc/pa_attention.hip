@@ -512,13 +512,16 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
       ti.kp = p.k + off;
       ti.vp = p.v + off;
     } else {
-      // segment holding tile `it`: the number of segments that end at or before it
-      const int gsel = __builtin_popcountll(__ballot(f_cum_end <= it));
-      const int cend = __shfl(f_cum_end, gsel, 64);
-      const int ntl = __shfl(f_tiles, gsel, 64);
-      const int ul = __shfl(f_used, gsel, 64);
-      const int64_t base = __shfl(f_base, gsel, 64);
-      ti.bias = __shfl(f_bias, gsel, 64);
+      // segment holding tile `it`: the number of segments that end at or before
+      // it.  The index is wave-uniform, so its fields are read with v_readlane
+      // (scalar reads, no LDS round trip on the way to the tile's loads).
+      const int gsel = __builtin_amdgcn_readfirstlane(__builtin_popcountll(__ballot(f_cum_end <= it)));
+      const int cend = __builtin_amdgcn_readlane(f_cum_end, gsel);
+      const int ntl = __builtin_amdgcn_readlane(f_tiles, gsel);
+      const int ul = __builtin_amdgcn_readlane(f_used, gsel);
+      const int64_t base = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(f_base >> 32), gsel) << 32) |
+                                     (uint32_t)__builtin_amdgcn_readlane((int)f_base, gsel));
+      ti.bias = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f_bias), gsel));
       const int lt = it - (cend - ntl);
       const int nv = ul - 16 * lt;
       ti.nvalid = nv > 16 ? 16 : nv;

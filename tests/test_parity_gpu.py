@@ -53,8 +53,14 @@ SMALL = {
                               window=40),
     "page1": dict(B=2, sq=1, Hq=4, Hkv=2, D=64, P=1, seq_lens=[5, 40]),
     "many_requests": dict(B=70, sq=1, Hq=8, Hkv=2, D=64, P=16, seq_lens=("uniform", 0, 200)),
+    # larger shapes: 300 requests of plain multi-head attention (G = 1), a 16-token block
+    # with G = 16 (256 rows: four row groups), and 1024-token pages (64 tiles per page)
+    "mha_300_requests": dict(B=300, sq=2, Hq=4, Hkv=4, D=64, P=16, seq_lens=("uniform", 0, 300)),
+    "block_sq16_g16": dict(B=2, sq=16, Hq=64, Hkv=4, D=128, P=16, seq_lens=[100, 1000],
+                           window=200),
+    "page1024": dict(B=2, sq=4, Hq=8, Hkv=2, D=64, P=1024, seq_lens=[1500, 3000]),
 }
-SPLITS = [1, 0, 3, -2]
+SPLITS = [1, 0, 3, -2, 64]
 
 
 def _small(name, seed=7):
