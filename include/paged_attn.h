@@ -3,13 +3,16 @@
  *
  * What it computes (vLLM API documentation pages):
  *   - vllm.v1.attention.backends.flashinfer_ts: attention of a uniform query
- *     block (query_len >= 1 tokens per request, grouped-query heads, dense
- *     non-causal mask) over a paged cache [pages, Hkv, page_size, 2*D] whose K
- *     and V are the two halves of each page row (module docstring "Layout",
- *     _kv_views), with an optional sliding window applied as a page-aligned
- *     suffix (module docstring "Sliding window", _restrict_to_window), and
- *     the fp8 scale folding of FlashInferTSImpl.forward (bmm1_scale =
- *     scale * k_scale, bmm2_scale = v_scale).
+ *     block (query_len >= 1 tokens per request, grouped-query heads) over a
+ *     paged cache [pages, Hkv, page_size, 2*D] whose K and V are the two
+ *     halves of each page row (module docstring "Layout", _kv_views): the
+ *     dense block with an optional sliding window applied as a page-aligned
+ *     suffix (module docstring "Sliding window", _restrict_to_window), or the
+ *     causal block with an exact per-token window (_get_plan: mask_type
+ *     "causal", window_left = window - 1); the fp8 scale folding of
+ *     FlashInferTSImpl.forward (bmm1_scale = scale * q_scale * k_scale,
+ *     bmm2_scale = v_scale); and the cache write that precedes the step
+ *     (do_kv_cache_update).
  *   - vllm.v1.attention.backends.fa_utils: Split-KV (num_splits) with a
  *     natural-log LSE returned per row and head (return_softmax_lse).
  *   - vllm.v1.attention.ops.dash_attention, flash_dash_attention: attention

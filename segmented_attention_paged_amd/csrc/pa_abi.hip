@@ -13,13 +13,11 @@
 #include "pa_kernels.h"
 #include "pa_plan.h"
 
-// waves per workgroup of the segment kernels (one 16-row query group per wave set)
-#ifndef PA_SEG_FUSED_WAVES
-#define PA_SEG_FUSED_WAVES 4
-#endif
-#ifndef PA_SEG_WAVES
-#define PA_SEG_WAVES 1
-#endif
+// Waves per workgroup of the segment kernels at one 16-row tile per wave: the
+// fused kernel splits a (query, kv head)'s tiles over 4 waves; the two-stage
+// kernel's items (one segment) are a few tiles long and take one wave.
+constexpr int kSegFusedWaves = 4;
+constexpr int kSegWaves = 1;
 
 using namespace pa;
 
@@ -418,7 +416,7 @@ int segment_attn_run(const void* q, int32_t q_dtype, const void* k, const void* 
   p.bs = bs;
   p.local = local;
   if (fused) {
-    const int NW = RT == 1 ? PA_SEG_FUSED_WAVES : 4 / RT;
+    const int NW = RT == 1 ? kSegFusedWaves : 4 / RT;
     p.items = N;
     p.out = out;
     p.out_kind = out_dtype;
@@ -436,7 +434,7 @@ int segment_attn_run(const void* q, int32_t q_dtype, const void* k, const void* 
   const int64_t rows = (int64_t)N * Gs * Hq;
   float* part_o = static_cast<float*>(workspace);
   float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * D * 4));
-  const int NW = RT == 1 ? PA_SEG_WAVES : 4 / RT;
+  const int NW = RT == 1 ? kSegWaves : 4 / RT;
   p.items = N * Gs;
   p.out = part_o;
   p.out_kind = PA_F32;
