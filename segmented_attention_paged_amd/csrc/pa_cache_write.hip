@@ -8,8 +8,8 @@
 // nearest finite e4m3fn value (ties to even, saturating at +-448, NaN kept),
 // so that scale * stored is what the attention kernels read back.
 //
-// One thread moves 8 consecutive values of one (token, kv head) row: a 16-byte
-// load and a 16-byte (8-byte for fp8) store.  The kernel is a pure HBM scatter.
+// The kernel is a pure HBM scatter: each thread moves a 16-byte (fp8: 32-byte)
+// piece of one (token, kv head) row.
 
 #include "pa_device.h"
 #include "pa_kernels.h"
@@ -46,27 +46,29 @@ __device__ __forceinline__ float to_f32(uint32_t half_bits) {
   return (float)bitcast<_Float16>((uint16_t)half_bits);
 }
 
-// WIDE: 64-bit thread and slot arithmetic (more than 2^31 threads or slots);
-// otherwise 32-bit divisions.
-template <int IN, bool FP8, bool WIDE>
+// One thread moves VPT consecutive values of one (token, kv head) row: VPT = 8
+// (a 16-byte load and store) for a 16-bit cache, 16 for an fp8 cache (two
+// 16-byte loads, one 16-byte store).  WIDE: 64-bit thread and slot arithmetic
+// (more than 2^31 threads or slots); otherwise 32-bit divisions.
+template <int IN, bool FP8, bool WIDE, int VPT>
 __global__ __launch_bounds__(256) void kv_write_kernel(KVWriteParams p) {
-  const int tpr = p.D / 4;  // threads per (token, head): 2D values, 8 per thread
-  int64_t row, tok, page, off;
+  static_assert(VPT == 8 || (FP8 && VPT == 16), "values per thread");
+  const int tpr = 2 * p.D / VPT;  // threads per (token, head)
+  int64_t tok, page, off;
   int e, h;
   if constexpr (WIDE) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    row = t / tpr;  // token * Hkv + head
+    const int64_t row = t / tpr;  // token * Hkv + head
     if (row >= (int64_t)p.T * p.Hkv) return;
-    e = (int)(t - row * tpr) * 8;
+    e = (int)(t - row * tpr) * VPT;
     tok = row / p.Hkv;
     h = (int)(row - tok * p.Hkv);
   } else {
     const uint32_t t = blockIdx.x * 256u + threadIdx.x;
     const uint32_t r32 = t / (uint32_t)tpr;
     if (r32 >= (uint32_t)p.T * (uint32_t)p.Hkv) return;
-    e = (int)(t - r32 * (uint32_t)tpr) * 8;
+    e = (int)(t - r32 * (uint32_t)tpr) * VPT;
     const uint32_t t32 = r32 / (uint32_t)p.Hkv;
-    row = r32;
     tok = t32;
     h = (int)(r32 - t32 * (uint32_t)p.Hkv);
   }
@@ -85,11 +87,13 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KVWriteParams p) {
   const int d = is_v ? e - p.D : e;
   const uint16_t* src = reinterpret_cast<const uint16_t*>(is_v ? p.value : p.key) +
                         tok * (is_v ? p.value_stride : p.key_stride) + (int64_t)h * p.D + d;
-  const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+  u32x4 x[VPT / 8];
+#pragma unroll
+  for (int c = 0; c < VPT / 8; ++c) x[c] = *reinterpret_cast<const u32x4*>(src + 8 * c);
   const int64_t dst_off = page * p.page_stride + (int64_t)h * p.head_stride + off * p.token_stride + d;
   if constexpr (!FP8) {
     char* dst = static_cast<char*>(is_v ? p.v_cache : p.k_cache) + dst_off * 2;
-    *reinterpret_cast<u32x4*>(dst) = x;
+    *reinterpret_cast<u32x4*>(dst) = x[0];
   } else {
     // x / scale rounded to fp32, computed as fp32(double(x) * RN64(1 / scale)).
     // This is the correctly rounded fp32 quotient: the product is within 2^-52
@@ -98,38 +102,46 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KVWriteParams p) {
     // (only quotients in the fp32 subnormal range escape the argument, and
     // they all encode to +-0 in e4m3fn either way).
     const double inv = is_v ? p.v_inv : p.k_inv;
-    uint32_t w[2] = {0u, 0u};
+    uint32_t w[VPT / 4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {  // values 2i, 2i+1 = the two halves of dword i
-      const float q0 = (float)((double)to_f32<IN>(x[i] & 0xFFFFu) * inv);
-      const float q1 = (float)((double)to_f32<IN>(x[i] >> 16) * inv);
-      w[i >> 1] |= e4m3fn_pair(q0, q1) << (16 * (i & 1));
+    for (int i = 0; i < VPT / 2; ++i) {  // values 2i, 2i+1 = the two halves of dword i
+      const uint32_t dw = x[i >> 2][i & 3];
+      const float q0 = (float)((double)to_f32<IN>(dw & 0xFFFFu) * inv);
+      const float q1 = (float)((double)to_f32<IN>(dw >> 16) * inv);
+      const uint32_t pair = e4m3fn_pair(q0, q1);
+      if (i & 1) w[i >> 1] |= pair << 16;
+      else w[i >> 1] = pair;
     }
     char* dst = static_cast<char*>(is_v ? p.v_cache : p.k_cache) + dst_off;
-    *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+    if constexpr (VPT == 16) *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+    else *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
   }
 }
 
-template <int IN, bool FP8>
-hipError_t launch_kv_write_t(const KVWriteParams& p, hipStream_t stream, int64_t grid) {
+template <int IN, bool FP8, int VPT>
+hipError_t launch_kv_write_t(const KVWriteParams& p, hipStream_t stream) {
+  const int64_t threads = (int64_t)p.T * p.Hkv * (2 * p.D / VPT);
+  if (threads == 0) return hipSuccess;
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (p.capacity > 0x7fffffffLL || grid * 256 > 0x7fffffffLL)
-    hipLaunchKernelGGL((kv_write_kernel<IN, FP8, true>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((kv_write_kernel<IN, FP8, true, VPT>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((kv_write_kernel<IN, FP8, false>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((kv_write_kernel<IN, FP8, false, VPT>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_kv_write(const KVWriteParams& p, int in_kind, int cache_kind, hipStream_t stream) {
-  const int64_t threads = (int64_t)p.T * p.Hkv * (p.D / 4);
-  if (threads == 0) return hipSuccess;
-  const int64_t grid = (threads + 255) / 256;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const bool fp8 = cache_kind == K_FP8;
-  if (in_kind == K_BF16)
-    return fp8 ? launch_kv_write_t<K_BF16, true>(p, stream, grid) : launch_kv_write_t<K_BF16, false>(p, stream, grid);
-  return fp8 ? launch_kv_write_t<K_FP16, true>(p, stream, grid) : launch_kv_write_t<K_FP16, false>(p, stream, grid);
+  const bool wide16 = fp8 && p.D % 16 == 0;  // fp8 rows in 16-value pieces
+  if (in_kind == K_BF16) {
+    if (!fp8) return launch_kv_write_t<K_BF16, false, 8>(p, stream);
+    return wide16 ? launch_kv_write_t<K_BF16, true, 16>(p, stream) : launch_kv_write_t<K_BF16, true, 8>(p, stream);
+  }
+  if (!fp8) return launch_kv_write_t<K_FP16, false, 8>(p, stream);
+  return wide16 ? launch_kv_write_t<K_FP16, true, 16>(p, stream) : launch_kv_write_t<K_FP16, true, 8>(p, stream);
 }
 
 }  // namespace pa
