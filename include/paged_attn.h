@@ -118,7 +118,8 @@ typedef struct pa_kv_desc {
  *             attention kernel and read by the combine kernel that follows it
  *             on `stream`.  Its contents need no initialization; calls that
  *             share a workspace must not overlap in time.
- * B == 0 or query_len == 0 is a no-op returning PA_OK.
+ * B == 0 or query_len == 0 is a no-op returning PA_OK.  B * query_len and
+ * (Hq / Hkv) * query_len must stay below 2^31 (PA_EINVAL otherwise).
  */
 int paged_attn_run(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
                    const int32_t* block_table, int64_t bt_row_stride, int32_t bt_width,
@@ -212,7 +213,8 @@ int segment_attn_combine(const void* part_o, int32_t part_dtype, const float* pa
  * (fused != 0) folds each segment's bias into one online softmax per
  * (query, kv head) and needs no workspace; otherwise the workspace holds the
  * [N, topk+1, Hq, D+1] fp32 partials (segment_attn_workspace_size bytes).
- * out [N, Hq, D] in out_dtype; lse [N, Hq] or NULL. */
+ * out [N, Hq, D] in out_dtype; lse [N, Hq] or NULL.  topk <= 63 and
+ * N * (topk + 1) < 2^31 (PA_EINVAL otherwise). */
 int segment_attn_run(const void* q, int32_t q_dtype, const void* k, const void* v,
                      int32_t kv_dtype, const int32_t* used, const float* bias, int32_t N,
                      int32_t topk, int32_t bs, int32_t local, int32_t Hq, int32_t Hkv,

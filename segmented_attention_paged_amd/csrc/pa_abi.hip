@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
 
 #include "../../include/paged_attn.h"
@@ -139,6 +140,9 @@ int check_paged(const void* q, int32_t q_dtype, const pa_kv_desc* kv, const int3
     return fail(PA_EINVAL, "kv strides must be non-negative multiples of 16 bytes");
   if (kv->token_stride * eb > (int64_t)1 << 26)  // lane offsets inside a tile are 32-bit
     return fail(PA_EINVAL, "token stride above 64 MiB");
+  // query rows (B*query_len) and rows per kv head ((Hq/Hkv)*query_len) are 32-bit counts
+  if ((int64_t)B * query_len > INT32_MAX || (int64_t)(Hq / kv->num_kv_heads) * query_len > INT32_MAX)
+    return fail(PA_EINVAL, "B*query_len and (Hq/Hkv)*query_len must be below 2^31");
   if (B == 0 || query_len == 0) return PA_OK;
   if (!q || !kv->k || !kv->v || !block_table || !seq_lens)
     return fail(PA_EINVAL, "NULL input pointer");
@@ -380,6 +384,7 @@ int segment_attn_run(const void* q, int32_t q_dtype, const void* k, const void* 
   if (bs % 8 || local % 8 || bs < 0 || local < 0)
     return fail(PA_EINVAL, "segments must be multiples of 8 rows (bs=%d, local=%d)", bs, local);
   if (N < 0 || topk < 0 || topk > 63) return fail(PA_EINVAL, "bad N or topk");
+  if ((int64_t)N * (topk + 1) > INT32_MAX) return fail(PA_EINVAL, "N*(topk+1) must be below 2^31");
   if (D != 64 && D != 128) return fail(PA_EINVAL, "head_dim must be 64 or 128");
   if (Hkv <= 0 || Hq <= 0 || Hq % Hkv) return fail(PA_EINVAL, "Hq must be a positive multiple of Hkv");
   if ((int64_t)Hkv * D * 2 > (int64_t)1 << 26) return fail(PA_EINVAL, "token stride above 64 MiB");

@@ -132,6 +132,9 @@ def test_argument_errors_are_status_codes():
     assert _run(desc=d) == _lib.PA_EINVAL
     assert _run(bt_stride=2) == _lib.PA_EINVAL
     assert _run(S=4, lens=16) == _lib.PA_EWORKSPACE
+    # row counts that would overflow 32-bit arithmetic
+    assert _run(B=1 << 16, sq=1 << 15) == _lib.PA_EINVAL and "2^31" in _lib.last_error()
+    assert _run(Hq=2 * 1024, sq=1 << 21) == _lib.PA_EINVAL  # (Hq/Hkv)*sq = 2^31
     # empty problems are no-ops
     assert _run(B=0, q=None, out=None) == _lib.PA_OK
     assert _run(sq=0, q=None, out=None) == _lib.PA_OK
@@ -151,3 +154,4 @@ def test_segment_argument_errors():
     assert seg(qd=_lib.PA_F32) == _lib.PA_ENOTSUP
     assert seg(fused=0) == _lib.PA_EWORKSPACE
     assert seg(N=0, q=None) == _lib.PA_OK
+    assert seg(N=1 << 26, topk=63) == _lib.PA_EINVAL and "2^31" in _lib.last_error()
