@@ -211,13 +211,12 @@ __device__ __forceinline__ void load_q(typename QTypes<QT>::QOp (&qf)[D / 32], c
 }
 
 // One 16-key tile against one 16-row tile: S^T, online softmax, O^T += V^T P^T.
-// load_v() fills f.vA when the caller has not yet (a no-op otherwise); it runs
-// after the rescale so that the V operands are not live across S and the max.
-template <int D, int QT, bool CAUSAL = false, typename LoadV>
-__device__ __forceinline__ void attend_tile(Frags<D, QT>& f, const typename QTypes<QT>::QOp (&qf)[D / 32],
+template <int D, int QT, bool CAUSAL = false>
+__device__ __forceinline__ void attend_tile(const Frags<D, QT>& f,
+                                            const typename QTypes<QT>::QOp (&qf)[D / 32],
                                             f32x4 (&acc)[D / 16], float& m_run, float& l_run,
                                             float scale_log2, float bias, int nvalid, int g4,
-                                            int key0, RowMask rm, LoadV&& load_v) {
+                                            int key0 = 0, RowMask rm = RowMask{false, 0, 0}) {
   f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kc = 0; kc < D / 32; ++kc) sacc = qk_mfma<QT>(f.kf[kc], qf[kc], sacc);
@@ -254,7 +253,6 @@ __device__ __forceinline__ void attend_tile(Frags<D, QT>& f, const typename QTyp
     for (int j = 0; j < D / 16; ++j) acc[j] *= alpha;
     m_run = m_new;
   }
-  load_v();
   // causal rows with no key so far have only -inf logits: any finite reference
   float m_ref = m_run;
   if constexpr (CAUSAL) m_ref = m_run == kNegInf ? 0.f : m_run;
@@ -576,13 +574,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
     hi_min = Lr - p.sq;
     lo_max = p.window_left >= 0 ? Lr - 1 - p.window_left : INT32_MIN;
   }
-  auto attend = [&](Frags<D, QT>& f, const TileInfo& ti) {
+  auto attend = [&](const Frags<D, QT>& f, const TileInfo& ti) {
     const bool on = CAUSAL && (ti.key0 + 15 > hi_min || ti.key0 < lo_max);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
       attend_tile<D, QT, CAUSAL>(f, qf[rt], acc[rt], m_run[rt], l_run[rt], p.qk_scale_log2,
                                  ti.bias, ti.nvalid, g4, ti.key0,
-                                 RowMask{on, row_hi[rt], row_lo[rt]}, [] {});
+                                 RowMask{on, row_hi[rt], row_lo[rt]});
   };
 
   // main loop: tile k+1 is in flight while tile k is computed
@@ -705,7 +703,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
 // j / (IPT / NW).
 // ================================================================================
 template <int D, int NW, int KV, int QT, int NBUF, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(5))) void attn_shared_kernel(const AttnParams p) {
+__global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p) {
   using G = Geo<D, KV>;
   constexpr int KB = G::KB;
   constexpr int VPL = G::VPL;
@@ -869,24 +867,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(5))) vo
       v_lds[pp] = 16 * (t * G::CPK + (cv ^ (t & G::SWZ))) + 8 * a;
     }
   }
-  auto read_k = [&](const char* st, Frags<D, QT>& f) {
+  auto read_frags = [&](auto sc, Frags<D, QT>& f) {
+    const char* st = stage_buf(sc);
     if constexpr (TR) {
 #pragma unroll
       for (int kc = 0; kc < G::NKC; ++kc) f.kf[kc] = *reinterpret_cast<const u32x4*>(st + k_lds[kc]);
-    } else {
-      u32x4 rk[G::KLD];
-#pragma unroll
-      for (int i = 0; i < G::KLD; ++i) rk[i] = *reinterpret_cast<const u32x4*>(st + k_lds[i]);
-      k_operands<D, KV, QT>(rk, f);
-    }
-  };
-  auto read_v = [&](const char* st, Frags<D, QT>& f) {
-    if constexpr (TR) {
 #pragma unroll
       for (int j = 0; j < VPL; ++j)
         f.vA[j] = bitcast<u32x2>(__builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(st + v_lds[j])));
     } else {
+      u32x4 rk[G::KLD];
+#pragma unroll
+      for (int i = 0; i < G::KLD; ++i) rk[i] = *reinterpret_cast<const u32x4*>(st + k_lds[i]);
+      k_operands<D, KV, QT>(rk, f);
       constexpr int PV = QTypes<QT>::PV;
 #pragma unroll
       for (int pp = 0; pp < VPL / 2; ++pp) {
@@ -959,12 +953,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(5))) vo
     const int nvalid = cursor_valid(cc);
     const int key0 = cc.tok0;
     advance(cc);
-    const char* st = stage_buf(sc);
     Frags<D, QT> f;
-    read_k(st, f);
+    read_frags(sc, f);
     const bool on = CAUSAL && (key0 + 15 > hi_min || key0 < lo_max);
     attend_tile<D, QT, CAUSAL>(f, qf, acc, m_run, l_run, p.qk_scale_log2, 0.f, nvalid, g4, key0,
-                               RowMask{on, row_hi, row_lo}, [&] { read_v(st, f); });
+                               RowMask{on, row_hi, row_lo});
     return true;
   };
   for (int k = 0;; k += NBUF)
