@@ -40,6 +40,29 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _need(t: Optional[torch.Tensor], name: str, shape=None, dtype=None, contiguous: bool = True):
+    """Raise ValueError / TypeError unless t (skipped when None) has this shape, dtype and a
+    dense row-major layout.  The kernels index these buffers from their shapes alone, so a
+    smaller or strided tensor would be read or written out of bounds."""
+    if t is None:
+        return
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_device(dev: torch.device, **tensors):
+    """Every given tensor must live on the GPU `dev` (a host pointer reaching a kernel faults)."""
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
 def kv_desc(k: torch.Tensor, v: torch.Tensor, *, k_scale: float = 1.0, v_scale: float = 1.0,
             num_pages: Optional[int] = None) -> PaKvDesc:
     """Descriptor of paged K/V views shaped [pages, Hkv, page_size, D] with any strides
@@ -84,6 +107,17 @@ def new_workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(((max(int(nbytes), 16) + 15) // 16) * 16, dtype=torch.uint8, device=device)
 
 
+def _check_paged_inputs(q, block_table, seq_lens):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, query_len, Hq, D]")
+    _need(q, "q")
+    B = q.shape[0]
+    if block_table.dim() != 2 or block_table.shape[0] != B or block_table.stride(1) != 1:
+        raise ValueError("block_table must be [B, W] with unit column stride")
+    _need(block_table, "block_table", dtype=torch.int32, contiguous=False)
+    _need(seq_lens, "seq_lens", (B,), torch.int32)
+
+
 def paged_attn_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_table: torch.Tensor,
                    seq_lens: torch.Tensor, *, scale: float, window: int = 0, num_splits: int = 0,
                    k_scale: float = 1.0, v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
@@ -96,16 +130,18 @@ def paged_attn_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_tabl
     (paged_attn_run_causal); otherwise the dense block with the page-aligned window.
     Returns (out [B, sq, Hq, D], lse [B, sq, Hq] fp32 natural log, or None)."""
     B, sq, Hq, D = q.shape
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous")
-    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
-        raise TypeError("block_table and seq_lens must be int32")
+    _check_paged_inputs(q, block_table, seq_lens)
     desc = kv_desc(k, v, k_scale=k_scale, v_scale=v_scale)
     if out is None:
         default = q.dtype if q.dtype in (torch.bfloat16, torch.float16) else torch.bfloat16
         out = torch.empty((B, sq, Hq, D), dtype=out_dtype or default, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, sq, Hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", (B, sq, Hq, D))
+    _need(lse, "lse", (B, sq, Hq), torch.float32)
+    _need(workspace, "workspace")
+    _same_device(q.device, k=k, v=v, block_table=block_table, seq_lens=seq_lens, out=out, lse=lse,
+                 workspace=workspace)
     W = block_table.shape[1]
     need = workspace_size(B, sq, Hq, desc.num_kv_heads, D, desc.page_size, W, window, num_splits)
     if need and workspace is None:
@@ -125,6 +161,7 @@ def paged_attn_partial(q, k, v, block_table, seq_lens, *, scale: float, num_spli
                        part_o: Optional[torch.Tensor] = None, part_lse: Optional[torch.Tensor] = None):
     """Split-KV partials: (part_o [S, B*sq, Hq, D] fp32, part_lse [S, B*sq, Hq] fp32)."""
     B, sq, Hq, D = q.shape
+    _check_paged_inputs(q, block_table, seq_lens)
     desc = kv_desc(k, v, k_scale=k_scale, v_scale=v_scale)
     W = block_table.shape[1]
     S = resolve_splits(B, sq, Hq, desc.num_kv_heads, D, desc.page_size, W, window, num_splits)
@@ -132,6 +169,10 @@ def paged_attn_partial(q, k, v, block_table, seq_lens, *, scale: float, num_spli
         part_o = torch.empty((S, B * sq, Hq, D), dtype=torch.float32, device=q.device)
     if part_lse is None:
         part_lse = torch.empty((S, B * sq, Hq), dtype=torch.float32, device=q.device)
+    _need(part_o, "part_o", (S, B * sq, Hq, D), torch.float32)
+    _need(part_lse, "part_lse", (S, B * sq, Hq), torch.float32)
+    _same_device(q.device, k=k, v=v, block_table=block_table, seq_lens=seq_lens, part_o=part_o,
+                 part_lse=part_lse)
     check(load().paged_attn_partial(
         q.data_ptr(), dtype_code(q.dtype), ctypes.byref(desc), block_table.data_ptr(),
         block_table.stride(0), W, seq_lens.data_ptr(), B, sq, Hq, D, float(scale), int(window),
@@ -143,9 +184,13 @@ def split_kv_combine(part_o: torch.Tensor, part_lse: torch.Tensor, *, out_dtype=
                      out: Optional[torch.Tensor] = None, return_lse: bool = True):
     """LSE-weighted merge of Split-KV partials [S, rows, Hq, D] -> (out [rows, Hq, D], lse)."""
     S, rows, Hq, D = part_o.shape
+    _need(part_o, "part_o", dtype=torch.float32)
+    _need(part_lse, "part_lse", (S, rows, Hq), torch.float32)
     if out is None:
         out = torch.empty((rows, Hq, D), dtype=out_dtype, device=part_o.device)
+    _need(out, "out", (rows, Hq, D))
     lse = torch.empty((rows, Hq), dtype=torch.float32, device=part_o.device) if return_lse else None
+    _same_device(part_o.device, part_lse=part_lse, out=out)
     check(load().split_kv_combine(part_o.data_ptr(), part_lse.data_ptr(), S, rows, Hq, D,
                                   out.data_ptr(), dtype_code(out.dtype), _ptr(lse),
                                   _stream(part_o.device)))
@@ -157,9 +202,17 @@ def segment_attn_combine(part_o: torch.Tensor, part_lse: torch.Tensor, used: tor
                          out: Optional[torch.Tensor] = None, return_lse: bool = True):
     """DASH combine of [N, G, Hq, D] partials with per-segment bias -> (out [N, Hq, D], lse)."""
     N, G, Hq, D = part_o.shape
+    _need(part_o, "part_o")
+    _need(part_lse, "part_lse", (N, G, Hq), torch.float32)
+    _need(used, "used", (N, G), torch.int32)
+    if G > 1 and bias is None:
+        raise ValueError("bias [N, G-1] is needed when there is more than one segment")
+    _need(bias, "bias", (N, G - 1), torch.float32)
     if out is None:
         out = torch.empty((N, Hq, D), dtype=out_dtype, device=part_o.device)
+    _need(out, "out", (N, Hq, D))
     lse = torch.empty((N, Hq), dtype=torch.float32, device=part_o.device) if return_lse else None
+    _same_device(part_o.device, part_lse=part_lse, used=used, bias=bias, out=out)
     check(load().segment_attn_combine(part_o.data_ptr(), dtype_code(part_o.dtype),
                                       part_lse.data_ptr(), used.data_ptr(), _ptr(bias), N, G, Hq, D,
                                       out.data_ptr(), dtype_code(out.dtype), _ptr(lse),
@@ -177,17 +230,28 @@ def segment_attn_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, used: to
                      return_lse: bool = True, out: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None):
     """DASH attention of q [N, Hq, D] over gathered segments k, v [N*(topk*bs+local), Hkv, D]."""
+    if q.dim() != 3 or bias.dim() != 2 or k.dim() != 3:
+        raise ValueError("q must be [N, Hq, D], bias [N, topk], k and v [tokens, Hkv, D]")
     N, Hq, D = q.shape
     topk = bias.shape[1]
     Hkv = k.shape[1]
+    tokens = N * (topk * int(bs) + int(local))
+    _need(q, "q")
+    _need(k, "k", (tokens, Hkv, D))
+    _need(v, "v", (tokens, Hkv, D), k.dtype)
+    _need(used, "used", (N, topk + 1), torch.int32)
+    _need(bias, "bias", (N, topk), torch.float32)
     if scale is None:
         scale = D ** -0.5
     if out is None:
         out = torch.empty((N, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    _need(out, "out", (N, Hq, D))
     lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device) if return_lse else None
     if not fused and workspace is None:
         workspace = torch.empty(segment_attn_workspace_size(N, topk, Hq, D), dtype=torch.uint8,
                                 device=q.device)
+    _need(workspace, "workspace")
+    _same_device(q.device, k=k, v=v, used=used, bias=bias, out=out, workspace=workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(load().segment_attn_run(
         q.data_ptr(), dtype_code(q.dtype), k.data_ptr(), v.data_ptr(), dtype_code(k.dtype),
@@ -212,6 +276,9 @@ def paged_kv_write(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.T
         raise ValueError("slot_mapping must be int64 [T]")
     desc = kv_desc(k, v, k_scale=k_scale, v_scale=v_scale)
     T, _, D = key.shape
+    if key.shape[1] != k.shape[1] or D != k.shape[3]:
+        raise ValueError("key/value [T, Hkv, D] must match the cache's kv heads and head_dim")
+    _same_device(key.device, value=value, slot_mapping=slot_mapping, k=k, v=v)
     check(load().paged_kv_write(key.data_ptr(), key.stride(0), value.data_ptr(), value.stride(0),
                                 dtype_code(key.dtype), T, D, slot_mapping.contiguous().data_ptr(),
                                 ctypes.byref(desc), _stream(key.device)))
@@ -222,7 +289,10 @@ def window_width(window: int, query_len: int, page_size: int, bt_width: int) -> 
 
 
 def _describe_shapes(block_table, query_len, Hq, Hkv, D, page_size, window, num_splits):
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be [B, W] with unit column stride")
     B, W = block_table.shape
+    _need(block_table, "block_table", dtype=torch.int32, contiguous=False)
     S = resolve_splits(B, query_len, Hq, Hkv, D, page_size, W, window, num_splits)
     ow = window_width(window, query_len, page_size, W)
     return B, W, S, ow
@@ -233,6 +303,8 @@ def paged_attn_describe(block_table, seq_lens, *, query_len, Hq, Hkv, D, page_si
     """Device integer plan: (lens [B], table [B, width], split_ranges [B, S, 4]) int32."""
     B, W, S, ow = _describe_shapes(block_table, query_len, Hq, Hkv, D, page_size, window, num_splits)
     dev = block_table.device
+    _need(seq_lens, "seq_lens", (B,), torch.int32)
+    _same_device(dev, seq_lens=seq_lens)
     lens = torch.empty(B, dtype=torch.int32, device=dev)
     table = torch.empty((B, ow), dtype=torch.int32, device=dev)
     ranges = torch.empty((B, S, 4), dtype=torch.int32, device=dev)
@@ -246,9 +318,12 @@ def paged_attn_describe(block_table, seq_lens, *, query_len, Hq, Hkv, D, page_si
 def paged_attn_describe_host(block_table, seq_lens, *, query_len, Hq, Hkv, D, page_size, window=0,
                              num_splits=0):
     """Same plan computed on the host from CPU int32 tensors (no GPU needed)."""
+    if block_table.device.type != "cpu" or seq_lens.device.type != "cpu":
+        raise ValueError("paged_attn_describe_host reads host memory: pass CPU tensors")
     block_table = block_table.contiguous()
     seq_lens = seq_lens.contiguous()
     B, W, S, ow = _describe_shapes(block_table, query_len, Hq, Hkv, D, page_size, window, num_splits)
+    _need(seq_lens, "seq_lens", (B,), torch.int32)
     lens = torch.empty(B, dtype=torch.int32)
     table = torch.empty((B, ow), dtype=torch.int32)
     ranges = torch.empty((B, S, 4), dtype=torch.int32)

@@ -8,8 +8,9 @@
 // nearest finite e4m3fn value (ties to even, saturating at +-448, NaN kept),
 // so that scale * stored is what the attention kernels read back.
 //
-// The kernel is a pure HBM scatter: each thread moves a 16-byte (fp8: 32-byte)
-// piece of one (token, kv head) row.
+// The kernel is a pure HBM scatter of pieces of one (token, kv head) row: 8
+// values per thread for a 16-bit cache (16 bytes in, 16 out), 16 for an fp8
+// cache when D is a multiple of 16 (32 bytes in, 16 out), else 8 (16 in, 8 out).
 
 #include "pa_device.h"
 #include "pa_kernels.h"
