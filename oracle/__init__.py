@@ -23,9 +23,11 @@ Pinning status of each function (the pins live in tests/test_oracle_*.py):
       points, torch float8_e4m3fn on all 256 bytes)
   paging.window_start_page, restrict_to_window ... pinned (hand-worked page
       examples, covering-suffix property, brute force)
-  paging.split_page_ranges ........................ parity unpinned (the pages
-      fix no split boundary rule; results downstream are rule-independent and
-      pinned by split-then-combine == unsplit)
+  paging.split_page_ranges ........................ pinned (brute force over
+      every in-order cut of up to 12 pages into up to 5 chunks: the cut with
+      the smallest largest chunk, filled front to back; partition invariants).
+      The pages fix no boundary rule: that selection is a reading, and results
+      downstream are rule-independent (split-then-combine == unsplit)
   attention.softmax_attention ..................... pinned (closed forms,
       brute force, torch SDPA in fp64, logaddexp)
   attention.paged_attention ....................... pinned (page permutation,

@@ -79,8 +79,10 @@ def split_page_ranges(n_pages: int, num_splits: int) -> list[tuple[int, int]]:
     ``FlashAttentionCuTeDSLCompileSpec``) but fix no boundary rule.  Reading
     taken here: equal page-granular chunks of ceil(n_pages / S) pages, in
     order; trailing chunks may be empty.  Returns (first_page, page_count)
-    relative to the first visible page.  Parity unpinned by the pages: the
-    combined result does not depend on this rule.
+    relative to the first visible page.  Among all in-order cuts into
+    num_splits chunks this is the one with the smallest largest chunk, filled
+    front to back (the brute-force pin in the tests).  The combined result
+    does not depend on the rule.
     """
     if num_splits < 1:
         raise ValueError("num_splits must be >= 1")

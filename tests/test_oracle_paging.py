@@ -90,3 +90,30 @@ def test_split_ranges_partition(n, S):
             assert first == cur
         cur += count
     assert cur == n
+
+
+def _compositions(n, S):
+    """Every way to cut n pages into S in-order chunks (sizes >= 0)."""
+    if S == 1:
+        yield (n,)
+        return
+    for first in range(n + 1):
+        for rest in _compositions(n - first, S - 1):
+            yield (first,) + rest
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 5])
+def test_split_ranges_brute_force(S):
+    # Reading R9 as a selection over all cuts: the smallest possible largest chunk
+    # (equal chunks), filled front to back (trailing chunks absorb the shortfall).
+    for n in range(0, 13):
+        cuts = list(_compositions(n, S))
+        best = min(max(c) for c in cuts)
+        chosen = max(c for c in cuts if max(c) == best)  # lexicographically largest
+        got = split_page_ranges(n, S)
+        assert tuple(count for _, count in got) == chosen, (n, S)
+        firsts = [0]
+        for c in chosen[:-1]:
+            firsts.append(firsts[-1] + c)
+        assert [first for first, count in got if count] == [f for f, c in zip(firsts, chosen) if c]
+
