@@ -155,3 +155,19 @@ def test_segment_argument_errors():
     assert seg(fused=0) == _lib.PA_EWORKSPACE
     assert seg(N=0, q=None) == _lib.PA_OK
     assert seg(N=1 << 26, topk=63) == _lib.PA_EINVAL and "2^31" in _lib.last_error()
+
+
+def test_missing_library_fails_loudly():
+    # a fresh interpreter pointed at a library that does not exist: the binding raises,
+    # it does not fall back to anything
+    import subprocess
+    import sys
+    code = ("import segmented_attention_paged_amd._lib as L\n"
+            "L.LIB_PATH = '/nonexistent/libsapaged.so'\n"
+            "try:\n"
+            "    L.load()\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert "raised:" in r.stdout and "is missing" in r.stdout, r.stdout + r.stderr
