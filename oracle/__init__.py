@@ -66,4 +66,4 @@ from .attention import (  # noqa: F401
     segment_attention,
     segment_attention_union,
 )
-from .cache_write import e4m3fn_encode, quantize_e4m3fn, write_kv_cache  # noqa: F401
+from .cache_write import convert_row, e4m3fn_encode, quantize_e4m3fn, write_kv_cache  # noqa: F401

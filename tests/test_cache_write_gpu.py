@@ -211,11 +211,12 @@ def test_write_then_attend(sap, kv_dtype):
     compare(out, lse, O, L, TOL_BF16 if kv_dtype == "bf16" else TOL_FP8)
 
 
-def test_full_size_sampled(sap):
+@pytest.mark.parametrize("cache_dtype", ["fp8_e4m3", "bf16"])
+def test_full_size_sampled(sap, cache_dtype):
     # the measured shape: 65536 tokens x 8 kv heads x D=128 into a 16-slot-page
-    # pool twice as large, fp8; 64 sampled tokens checked against the oracle,
-    # every untouched slot checked unchanged
-    w = make_kv_write(T=65536, Hkv=8, D=128, P=16, pages=8192, seed=40, cache_dtype="fp8_e4m3",
+    # pool twice as large; 64 sampled tokens checked against the oracle, every
+    # untouched slot checked unchanged
+    w = make_kv_write(T=65536, Hkv=8, D=128, P=16, pages=8192, seed=40, cache_dtype=cache_dtype,
                       pad_frac=0.05, device=DEV)
     before = w.cache.clone()
     sap.paged_kv_write(w.key, w.value, w.slot_mapping, *sap.kv_halves(w.cache, w.D),
@@ -231,8 +232,8 @@ def test_full_size_sampled(sap):
     rng = np.random.default_rng(2)
     for t in rng.choice(np.flatnonzero(slots >= 0), size=64, replace=False):
         s = int(slots[t])
-        kq = oracle.quantize_e4m3fn(oracle.bf16_to_f64(to_numpy_bits(w.key[t].cpu())), w.k_scale)
-        vq = oracle.quantize_e4m3fn(oracle.bf16_to_f64(to_numpy_bits(w.value[t].cpu())), w.v_scale)
+        kq = oracle.convert_row(to_numpy_bits(w.key[t].cpu()), "bf16", cache_dtype, w.k_scale)
+        vq = oracle.convert_row(to_numpy_bits(w.value[t].cpu()), "bf16", cache_dtype, w.v_scale)
         row = to_numpy_bits(w.cache[s // w.P, :, s % w.P].cpu())
         np.testing.assert_array_equal(row[:, : w.D], kq)
         np.testing.assert_array_equal(row[:, w.D:], vq)

@@ -27,21 +27,25 @@ def sap():
     return m
 
 
-@pytest.mark.parametrize("name", ["c2_gqa_decode", "c3_query_block", "c3w_query_block_window",
-                                  "c4_split_kv", "c4f_split_kv_fp8"])
-def test_full_size_sampled(sap, name):
+@pytest.mark.parametrize("name,causal", [
+    ("c1_tiny", False), ("c2_gqa_decode", False), ("c3_query_block", False),
+    ("c3w_query_block_window", False), ("c4_split_kv", False), ("c4f_split_kv_fp8", False),
+    # the blocks the bench also times with the causal mask, and with fp8 queries
+    ("c3_query_block", True), ("c3w_query_block_window", True), ("c3f_query_block_fp8", False),
+])
+def test_full_size_sampled(sap, name, causal):
     inp = paged_config(name, poison=True, device=DEV)
-    out, lse = run_paged(inp)  # the config's own num_splits (0 = library choice, C4: 16)
+    out, lse = run_paged(inp, causal=causal)  # the config's own num_splits (0 = library choice)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
     lens = inp.seq_lens.cpu()
     reqs = sorted({int(torch.argmin(lens)), int(torch.argmax(lens)), inp.B // 2})
     heads = sorted({0, inp.Hkv - 1})
-    O, L = oracle_paged(inp, requests=reqs, kv_heads=heads)
+    O, L = oracle_paged(inp, requests=reqs, kv_heads=heads, causal=causal)
     mask = ~np.isnan(L)
     assert mask.sum() == len(reqs) * len(heads) * (inp.Hq // inp.Hkv) * inp.sq
     tol = TOL_FP8 if inp.kv_dtype == "fp8_e4m3" else TOL_BF16
-    compare(out, lse, O, L, tol, mask=mask, what=name)
+    compare(out, lse, O, L, tol, mask=mask, what=f"{name} causal={causal}")
 
 
 @pytest.mark.parametrize("fused", [True, False])
