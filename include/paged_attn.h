@@ -50,7 +50,7 @@ enum pa_dtype { PA_BF16 = 1, PA_FP16 = 2, PA_FP8_E4M3 = 3, PA_F32 = 4 };
 enum pa_status {
   PA_OK = 0,
   PA_EINVAL = -1,     /* malformed argument (shape, stride, pointer, alignment) */
-  PA_ENOTSUP = -2,    /* well-formed but unsupported (dtype combination, head_dim) */
+  PA_ENOTSUP = -2,    /* well-formed but unsupported (dtype or dtype combination) */
   PA_EWORKSPACE = -3, /* workspace missing or smaller than *_workspace_size() */
   PA_EHIP = -4        /* a kernel launch failed; see pa_last_error() */
 };
@@ -84,8 +84,8 @@ typedef struct pa_kv_desc {
  *
  * q           [B, query_len, Hq, D] contiguous, q_dtype PA_BF16 | PA_FP16 |
  *             PA_FP8_E4M3.  A 16-bit cache must have the query's dtype; an
- *             fp8 cache takes either 16-bit query (K and V are decoded exactly
- *             to that type) or an fp8 query (flashinfer_ts keeps q and K/V
+ *             fp8 cache takes either a 16-bit query (K and V are decoded
+ *             exactly to that type) or an fp8 query (flashinfer_ts keeps q and K/V
  *             dtypes matched; the query arrives quantized): q.k then runs on
  *             fp8 MFMA and P.V in bf16.  An fp8 query's own scale is folded
  *             into `scale` by the caller (the page's bmm1_scale = scale *
@@ -180,7 +180,8 @@ int paged_attn_partial(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
  *   LSE = ln sum_{live s} exp(part_lse[s]);  O = sum_{live s} exp(part_lse[s] - LSE) part_o[s]
  * with live meaning part_lse[s] > -inf; no live split gives O = 0, LSE = -inf.
  * This is the segment combine of the dash_attention page with zero bias.
- * part_o [S, rows, Hq, D] fp32 (dead entries are not read), part_lse
+ * part_o [S, rows, Hq, D] fp32 (dead entries may hold anything, NaN included:
+ * they are loaded but never reach the result), part_lse
  * [S, rows, Hq] fp32; out [rows, Hq, D] in out_dtype; lse [rows, Hq] or NULL. */
 int split_kv_combine(const float* part_o, const float* part_lse, int32_t S, int32_t rows,
                      int32_t Hq, int32_t D, void* out, int32_t out_dtype, float* lse,
@@ -192,7 +193,8 @@ int split_kv_combine(const float* part_o, const float* part_lse, int32_t S, int3
  *   w = softmax over live g of (part_lse[n, g, h] + prior_g)   (all dead: w = 0)
  *   out[n, h] = sum_{live g} w_g part_o[n, g, h]
  * part_o [N, G, Hq, D] in part_dtype (PA_BF16 | PA_FP16 | PA_F32; dead
- * entries are not read), part_lse [N, G, Hq] fp32, used [N, G] int32,
+ * entries may hold anything: they never reach the result), part_lse
+ * [N, G, Hq] fp32, used [N, G] int32,
  * bias [N, G-1] fp32 (may be NULL when G == 1); out [N, Hq, D] in out_dtype;
  * lse [N, Hq] (logsumexp of the live part_lse + prior, -inf if none) or NULL. */
 int segment_attn_combine(const void* part_o, int32_t part_dtype, const float* part_lse,
@@ -213,14 +215,15 @@ int segment_attn_combine(const void* part_o, int32_t part_dtype, const float* pa
  * (fused != 0) folds each segment's bias into one online softmax per
  * (query, kv head) and needs no workspace; otherwise the workspace holds the
  * [N, topk+1, Hq, D+1] fp32 partials (segment_attn_workspace_size bytes).
- * out [N, Hq, D] in out_dtype; lse [N, Hq] or NULL.  topk <= 63 and
- * N * (topk + 1) < 2^31 (PA_EINVAL otherwise). */
+ * out [N, Hq, D] in out_dtype; lse [N, Hq] or NULL.  q, k, v and out are
+ * 16-byte aligned; topk <= 63 and N * (topk + 1) < 2^31 (PA_EINVAL otherwise). */
 int segment_attn_run(const void* q, int32_t q_dtype, const void* k, const void* v,
                      int32_t kv_dtype, const int32_t* used, const float* bias, int32_t N,
                      int32_t topk, int32_t bs, int32_t local, int32_t Hq, int32_t Hkv,
                      int32_t D, float scale, int32_t fused, void* out, int32_t out_dtype,
                      float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of workspace segment_attn_run needs with fused == 0 (0 for an empty problem). */
 size_t segment_attn_workspace_size(int32_t N, int32_t topk, int32_t Hq, int32_t D);
 
 /* Columns of the window-restricted block table (flashinfer_ts, _window_pages):
