@@ -302,8 +302,8 @@ def main(argv=None) -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures a single GPU: the path is built and measured on one MI355X; "
-              "multi-GPU runs (--gpus > 1) are not part of this build.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path, so --gpus > 1 "
+              "is not supported.", file=sys.stderr)
         return 2
 
     import torch
