@@ -39,11 +39,13 @@ __host__ __device__ inline SeqView seq_view(int32_t L, int32_t window, int32_t q
   return v;
 }
 
-// Columns of the restricted table (flashinfer_ts, _window_pages).
+// Columns of the restricted table (flashinfer_ts, _window_pages), saturating at
+// INT32_MAX for windows of about 2^31 keys over tiny pages.
 __host__ __device__ inline int32_t window_width(int32_t window, int32_t query_len, int32_t P,
                                                 int32_t bt_width) {
   if (window <= 0) return bt_width;
-  return (int32_t)cdiv64((int64_t)window + query_len - 1, P) + 1;
+  const int64_t w = cdiv64((int64_t)window + query_len - 1, P) + 1;
+  return (int32_t)(w < INT32_MAX ? w : INT32_MAX);
 }
 
 // Column of the caller's table that restricted column j reads (clamped to

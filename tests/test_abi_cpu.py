@@ -98,8 +98,12 @@ def test_auto_splits_are_valid():
 
 
 def test_window_width_matches_oracle():
-    for w, sq, P, W in [(0, 4, 16, 99), (4096, 16, 16, 2048), (20, 4, 16, 7), (1, 1, 16, 3)]:
+    for w, sq, P, W in [(0, 4, 16, 99), (4096, 16, 16, 2048), (20, 4, 16, 7), (1, 1, 16, 3),
+                        (2**31 - 1, 1, 16, 5)]:
         assert sap.window_width(w, sq, P, W) == oracle.window_table_width(w, sq, P, W)
+    # a width past int32 saturates instead of wrapping negative
+    assert oracle.window_table_width(2**31 - 1, 8, 1, 5) > 2**31 - 1
+    assert sap.window_width(2**31 - 1, 8, 1, 5) == 2**31 - 1
 
 
 def _desc(dtype=_lib.PA_BF16, D=128, P=16, hkv=2):
