@@ -282,6 +282,7 @@ SEG = {
     "seg_small": dict(N=6, Hq=8, Hkv=2, D=128, topk=3, bs=16, local=32),
     "seg_unaligned": dict(N=4, Hq=16, Hkv=4, D=64, topk=2, bs=8, local=24),
     "seg_g8": dict(N=3, Hq=32, Hkv=4, D=128, topk=8, bs=64, local=128),
+    "seg_g32": dict(N=3, Hq=32, Hkv=1, D=128, topk=4, bs=16, local=40),  # 32-row groups
 }
 
 
