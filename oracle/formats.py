@@ -22,7 +22,8 @@ import numpy as np
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     """bf16 bit patterns (uint16) -> exact fp64 values."""
     b = np.asarray(bits).astype(np.uint32) << np.uint32(16)
-    return b.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns widen to NaN, quietly
+        return b.view(np.float32).astype(np.float64)
 
 
 def fp16_to_f64(bits: np.ndarray) -> np.ndarray:
