@@ -5,18 +5,21 @@
 // tiles.  Keys are consumed in tiles of 16 slots of one page.
 //
 // Per 16-key tile and 16-row tile:
-//   S^T = K Q^T      D/32 x v_mfma_f32_16x16x32_{bf16,f16}; K is the A operand
-//                    (lane l: key l%16, 16 contiguous bytes of its row).
+//   S^T = K Q^T      D/32 x v_mfma_f32_16x16x32_{bf16,f16}, or _fp8_fp8 on the
+//                    stored bytes of K and q for an fp8 query; K is the A
+//                    operand (lane l: key l%16, 16 contiguous bytes of its row).
 //   online softmax   fp32 registers, log2 domain, v_exp_f32.
 //   O^T += V^T P^T   D/16 x v_mfma_f32_16x16x16_{bf16,f16}; P^T is the S^T
 //                    accumulator re-packed to 16 bits in place (same lane
-//                    layout); V^T comes from 4 keys x VPL head-dim values per
-//                    lane with 16-bit permutes: A-row m of MFMA j is head-dim
-//                    VPL*m + j.
-// fp8 (e4m3fn) K/V are decoded exactly to the query's 16-bit type with the
-// gfx950 pk conversions; k_scale folds into the logit scale and v_scale into
-// the epilogue (vllm.v1.attention.backends.flashinfer_ts, forward:
-// bmm1_scale / bmm2_scale).
+//                    layout).  V^T: in attn_kernel from 4 keys x VPL head-dim
+//                    values per lane with 16-bit permutes (A-row m of MFMA j is
+//                    head-dim VPL*m + j); in attn_shared_kernel from transposing
+//                    LDS reads (A-row m of MFMA j is head-dim 16*j + m).
+// fp8 (e4m3fn) K/V are decoded exactly to the 16-bit P.V type with the gfx950
+// pk conversions (K too, unless the query is fp8); k_scale folds into the logit
+// scale and v_scale into the epilogue (vllm.v1.attention.backends.flashinfer_ts,
+// forward: bmm1_scale / bmm2_scale).  Both kernels also come in a causal form:
+// bottom-right causal rows with an exact per-token window.
 //
 // Two kernels:
 //   attn_kernel         waves of a workgroup split the KEYS (round-robin
