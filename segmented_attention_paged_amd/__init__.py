@@ -8,6 +8,12 @@ on first use and raise if it is missing.
 
 from .api import (  # noqa: F401
     PagedAttnError,
+    pa_last_error,
+    pa_version,
+    paged_attn_plan,
+    paged_attn_resolve_splits,
+    paged_attn_window_width,
+    paged_attn_workspace_size,
     dtype_code,
     kv_desc,
     kv_halves,
@@ -15,6 +21,7 @@ from .api import (  # noqa: F401
     paged_attn_describe_host,
     paged_attn_partial,
     paged_attn_run,
+    paged_attn_run_causal,
     paged_kv_write,
     plan,
     resolve_splits,

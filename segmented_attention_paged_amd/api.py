@@ -156,6 +156,12 @@ def paged_attn_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_tabl
     return out, lse
 
 
+def paged_attn_run_causal(q, k, v, block_table, seq_lens, **kw):
+    """paged_attn_run with the bottom-right causal mask and an exact per-token window
+    (the C entry point paged_attn_run_causal); same arguments and results."""
+    return paged_attn_run(q, k, v, block_table, seq_lens, causal=True, **kw)
+
+
 def paged_attn_partial(q, k, v, block_table, seq_lens, *, scale: float, num_splits: int,
                        window: int = 0, k_scale: float = 1.0, v_scale: float = 1.0,
                        part_o: Optional[torch.Tensor] = None, part_lse: Optional[torch.Tensor] = None):
@@ -334,11 +340,28 @@ def paged_attn_describe_host(block_table, seq_lens, *, query_len, Hq, Hkv, D, pa
     return lens, table, ranges
 
 
+def pa_last_error() -> str:
+    """Message of the last failing library call on this thread."""
+    return _lib.last_error()
+
+
+def pa_version() -> str:
+    return load().pa_version().decode()
+
+
+# the C entry points' own names for the planning helpers
+paged_attn_plan = plan
+paged_attn_resolve_splits = resolve_splits
+paged_attn_workspace_size = workspace_size
+paged_attn_window_width = window_width
+
 __all__ = [
     "PagedAttnError", "dtype_code", "kv_desc", "kv_halves", "resolve_splits", "workspace_size", "plan",
     "new_workspace",
-    "paged_attn_run", "paged_attn_partial", "split_kv_combine", "segment_attn_combine",
+    "paged_attn_run", "paged_attn_run_causal", "paged_attn_partial", "split_kv_combine",
+    "segment_attn_combine", "paged_kv_write",
     "segment_attn_run", "segment_attn_workspace_size", "window_width", "paged_attn_describe",
-    "paged_attn_describe_host",
+    "paged_attn_describe_host", "paged_attn_plan", "paged_attn_resolve_splits",
+    "paged_attn_workspace_size", "paged_attn_window_width", "pa_last_error", "pa_version",
 ]
 PagedAttnError = _lib.PagedAttnError

@@ -39,6 +39,15 @@ def test_every_declared_symbol_is_exported_and_bound():
     assert set(_lib.SIGNATURES) == set(names)
 
 
+def test_binding_has_every_entry_point_by_name():
+    # the Python binding mirrors the C ABI name for name
+    for n in declared_functions():
+        assert callable(getattr(sap, n, None)), f"segmented_attention_paged_amd.{n} is missing"
+    assert sap.pa_version() == LIB.pa_version().decode()
+    assert sap.paged_attn_plan(64, 1, 32, 8, 128, 16, 512)["splits"] == sap.resolve_splits(
+        64, 1, 32, 8, 128, 16, 512)
+
+
 def test_version_and_last_error():
     assert b"gfx950" in LIB.pa_version()
     assert isinstance(LIB.pa_last_error(), bytes)

@@ -84,3 +84,16 @@ def test_causal_full_size_sampled(sap, name, window):
     O, L = oracle_paged(inp, requests=reqs, kv_heads=heads, window=window, causal=True)
     mask = ~np.isnan(L)
     compare(out, lse, O, L, TOL_BF16, mask=mask, what=f"{name} causal")
+
+
+def test_causal_entry_point_by_name(sap):
+    # the binding's paged_attn_run_causal is the C entry point of that name
+    inp = make_paged(B=2, sq=4, Hq=8, Hkv=2, D=128, P=16, seq_lens=[37, 90], seed=61).to(DEV)
+    k, v = sap.kv_halves(inp.cache, inp.D)
+    a = sap.paged_attn_run_causal(inp.q, k, v, inp.block_table, inp.seq_lens, scale=inp.scale,
+                                  window=20)
+    b = sap.paged_attn_run(inp.q, k, v, inp.block_table, inp.seq_lens, scale=inp.scale, window=20,
+                           causal=True)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
+    O, L = oracle_paged(inp, window=20, causal=True)
+    compare(*a, O, L, TOL_BF16, what="paged_attn_run_causal")
