@@ -56,7 +56,23 @@ struct Geo {
   static constexpr int VDW = VB / 4;                // ... in dwords
   static constexpr int RB = 2 * D * KB;             // bytes of one key's K and V in a staged tile
   static constexpr int CPK = RB / 16;               // 16-byte chunks per staged key
-  static constexpr int SWZ = CPK / 2 - 1;           // chunk swizzle mask (stays inside K or V)
+  static constexpr int SWZ = CPK / 2 - 1;           // chunk swizzle mask within the K or V half
+  // XOR applied to the chunk numbers of key t in a staged tile: t for K
+  // chunks; 2t for the V chunks of a 16-bit cache, so that the transposing V
+  // reads of one half-wave (keys t..t+7, two adjacent chunks each) land on 16
+  // distinct chunk positions instead of 8.
+  __device__ static int swz(int t, int c) {
+    if constexpr (KV == K_FP8 && CPK == 16) {
+      // 256-byte rows: a mask that also swaps the K and V halves of keys
+      // 4..7 and 12..15 (bit 3), so the K reads and the 8-bit transposing V
+      // reads each cover every bank instead of the half their chunks sit in
+      return ((2 * t) & 6) | (((t >> 2) ^ (t >> 3)) & 1) | (((t >> 2) & 1) << 3);
+    }
+    if (KV != K_FP8 && c >= CPK / 2) return (2 * t) & SWZ;
+    return t & SWZ;
+  }
+  // LDS chunk position of chunk c of key t (an involution within the key row)
+  __device__ static int chunk_pos(int t, int c) { return t * CPK + (c ^ swz(t, c)); }
   static constexpr int TILE_BYTES = 16 * RB;
   static constexpr int IPT = TILE_BYTES / 1024;     // 1 KiB direct-to-LDS loads per tile
 };
@@ -699,11 +715,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
 //
 // LDS ring: stage s holds one tile as 16 keys x CPK 16-byte chunks, K chunks
 // first then V chunks of each key, chunk c of key t stored at position
-// t*CPK + (c ^ (t & SWZ)).  The XOR keeps the K-operand reads (16 keys, same
-// chunk) on distinct banks; direct-to-LDS loads write lane i's 16 bytes to
-// position 64*j + i of instruction j, so each lane simply fetches the chunk
-// that belongs at its position.  Instruction j of a tile is issued by wave
-// j / (IPT / NW).
+// Geo::chunk_pos(t, c) = t*CPK + (c ^ Geo::swz(t, c)).  The XOR keeps the
+// K-operand reads (16 keys, same chunk) and the transposing V reads (two
+// adjacent chunks of 4 keys per 16-lane group) on distinct banks (no
+// conflicts with 32 or with 64 four-byte banks); direct-to-LDS loads write
+// lane i's 16 bytes to position 64*j + i of instruction j, so each lane simply
+// fetches the chunk that belongs at its position.  Instruction j of a tile is
+// issued by wave j / (IPT / NW).
 // ================================================================================
 template <int D, int NW, int KV, int QT, int NBUF, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p) {
@@ -782,7 +800,7 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
   for (int u = 0; u < IPW; ++u) {
     const int pos = 64 * (wave * IPW + u) + lane;
     const int t = pos / G::CPK;
-    const int c = (pos % G::CPK) ^ (t & G::SWZ);
+    const int c = (pos % G::CPK) ^ G::swz(t, pos % G::CPK);  // chunk_pos is an involution per key
     src_slot0[u] = c < G::CPK / 2 ? 16 * c : vk + 16 * (c - G::CPK / 2);
     src_key_off[u] = t * ts_b;
     src_key[u] = t;
@@ -852,14 +870,14 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
 #pragma unroll
   for (int i = 0; i < G::KLD; ++i) {
     const int t = c16, c = 4 * i + g4;
-    k_lds[i] = 16 * (t * G::CPK + (c ^ (t & G::SWZ)));
+    k_lds[i] = 16 * G::chunk_pos(t, c);
   }
   if constexpr (TR) {
     const int t = 4 * g4 + (c16 >> 2), a = c16 & 3;
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       const int cv = G::CPK / 2 + 2 * j + (a >> 1);  // 32 bytes of V per j, 8 per a
-      v_lds[j] = 16 * (t * G::CPK + (cv ^ (t & G::SWZ))) + 8 * (a & 1);
+      v_lds[j] = 16 * G::chunk_pos(t, cv) + 8 * (a & 1);
     }
   } else {
     const int e = c16 >> 1, a = c16 & 1;
@@ -867,7 +885,7 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
 #pragma unroll
     for (int pp = 0; pp < VPL / 2; ++pp) {
       const int cv = G::CPK / 2 + 2 * pp + (e >> 2);  // 16 bytes of V per PV MFMA
-      v_lds[pp] = 16 * (t * G::CPK + (cv ^ (t & G::SWZ))) + 8 * a;
+      v_lds[pp] = 16 * G::chunk_pos(t, cv) + 8 * a;
     }
   }
   auto read_frags = [&](auto sc, Frags<D, QT>& f) {
