@@ -554,6 +554,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   // Tile bases are wave-uniform (scalar registers); lanes add 32-bit offsets,
   // so each load is a scalar base plus one VGPR offset.
   const uint32_t tsb = (uint32_t)ts_b;  // 16 * tsb < 2^31 (checked at the boundary)
+  // 8 bytes of V per key and lane (fp8 with D = 128, 16-bit with D = 64): V
+  // arrives as two 16-byte loads per lane instead of four 8-byte ones (fewer
+  // load instructions per tile: fp8 Split-KV decode 358 -> 347 us)
+  constexpr bool kPairV = G::VDW == 2;
   auto load_tile = [&](Raw<D, KV>& r, const TileInfo& ti) {
     // offsets from the kernel-argument pointers keep the global address space
     const char* kb = p.k + uniform64(ti.kp - p.k);
@@ -562,11 +566,51 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
     const uint32_t koff = ks * tsb + 16 * g4;
 #pragma unroll
     for (int i = 0; i < G::KLD; ++i) r.k[i] = stream_load16(kb + (koff + 64 * i));
+    if constexpr (kPairV) {
+      // 16-byte V loads: the lane pair (2m, 2m+1) loads head dims 16m .. 16m+15
+      // of keys 4*(l/16) + {0, 1} (even lane) and {2, 3} (odd lane); pair_v
+      // swaps halves before use so each lane holds its 8 dims of all 4 keys
+      const int h = c16 & 1;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int key = 4 * g4 + 2 * h + i;
+        const uint32_t vs = key < ti.nvalid ? key : 0;
+        const u32x4 x = stream_load16(vb + (vs * tsb + 16 * (c16 >> 1)));
+        r.v[2 * i][0] = x[0];
+        r.v[2 * i][1] = x[1];
+        r.v[2 * i + 1][0] = x[2];
+        r.v[2 * i + 1][1] = x[3];
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t vs = 4 * g4 + i < ti.nvalid ? 4 * g4 + i : 0;
       load_v<G::VDW>(r.v[i], vb + (vs * tsb + G::VB * c16));
     }
+  };
+  // Lane-pair exchange after 16-byte V loads (see load_tile): afterwards
+  // r.v[i] holds head dims 8*(l%16) .. +7 of key 4*(l/16) + i, as the 8-byte
+  // loads deliver them.
+  auto pair_v = [&](Raw<D, KV>& r) {
+    const bool odd = (c16 & 1) != 0;
+    uint32_t keep[2][2], send[2][2], recv[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        keep[i][w] = odd ? r.v[2 * i + 1][w] : r.v[2 * i][w];
+        send[i][w] = odd ? r.v[2 * i][w] : r.v[2 * i + 1][w];
+        // quad_perm(1, 0, 3, 2): lanes 2m and 2m+1 swap
+        recv[i][w] = (uint32_t)__builtin_amdgcn_mov_dpp((int)send[i][w], 0xB1, 0xF, 0xF, false);
+      }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        r.v[i][w] = odd ? recv[i][w] : keep[i][w];
+        r.v[2 + i][w] = odd ? keep[i][w] : recv[i][w];
+      }
   };
 
   f32x4 acc[RT][VPL];
@@ -616,6 +660,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
         load_tile(nxt, tn);
       }
       Frags<D, QT> f;
+      if constexpr (kPairV) pair_v(cur);
       make_frags<D, KV, QT>(cur, f);
       attend(f, ti);
       if (!more) break;
