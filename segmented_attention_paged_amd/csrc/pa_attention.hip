@@ -45,6 +45,10 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;  // log2 units: softmax terms stay <= 256 before a rescale
+// attend_tile's optional hook, run right after the S^T MFMAs are issued
+struct NoHook {
+  __device__ void operator()() const {}
+};
 
 template <int D, int KV>
 struct Geo {
@@ -230,15 +234,21 @@ __device__ __forceinline__ void load_q(typename QTypes<QT>::QOp (&qf)[D / 32], c
 }
 
 // One 16-key tile against one 16-row tile: S^T, online softmax, O^T += V^T P^T.
-template <int D, int QT, bool CAUSAL = false>
+template <int D, int QT, bool CAUSAL = false, typename Hook = NoHook>
 __device__ __forceinline__ void attend_tile(const Frags<D, QT>& f,
                                             const typename QTypes<QT>::QOp (&qf)[D / 32],
                                             f32x4 (&acc)[D / 16], float& m_run, float& l_run,
                                             float scale_log2, float bias, int nvalid, int g4,
-                                            int key0 = 0, RowMask rm = RowMask{false, 0, 0}) {
+                                            int key0 = 0, RowMask rm = RowMask{false, 0, 0},
+                                            const Hook& mid = Hook{}) {
   f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kc = 0; kc < D / 32; ++kc) sacc = qk_mfma<QT>(f.kf[kc], qf[kc], sacc);
+  if constexpr (!std::is_same<Hook, NoHook>::value) {
+    __builtin_amdgcn_sched_barrier(0);
+    mid();
+    __builtin_amdgcn_sched_barrier(0);
+  }
   float s[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) s[i] = sacc[i] * scale_log2 + bias;
@@ -1012,10 +1022,16 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (k + NBUF - 1 < n_tiles) {
-      issue_tile(k + NBUF - 1, ci, std::integral_constant<int, (s + NBUF - 1) % NBUF>{});
-      advance(ci);
-    }
+    // Refill tile k-1's stage with tile k+NBUF-1, issued from inside tile k's
+    // work right after its S^T MFMAs: a wave issuing ring loads can stall while
+    // the memory system pushes back, and its MFMAs then run meanwhile (the
+    // fp8-query block measured 2-3% faster than issuing right after the barrier).
+    auto refill = [&]() {
+      if (k + NBUF - 1 < n_tiles) {
+        issue_tile(k + NBUF - 1, ci, std::integral_constant<int, (s + NBUF - 1) % NBUF>{});
+        advance(ci);
+      }
+    };
     const int nvalid = cursor_valid(cc);
     const int key0 = cc.tok0;
     advance(cc);
@@ -1023,7 +1039,7 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
     read_frags(sc, f);
     const bool on = CAUSAL && (key0 + 15 > hi_min || key0 < lo_max);
     attend_tile<D, QT, CAUSAL>(f, qf, acc, m_run, l_run, p.qk_scale_log2, 0.f, nvalid, g4, key0,
-                               RowMask{on, row_hi, row_lo});
+                               RowMask{on, row_hi, row_lo}, refill);
     return true;
   };
   for (int k = 0;; k += NBUF)
