@@ -45,7 +45,8 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;  // log2 units: softmax terms stay <= 256 before a rescale
-// attend_tile's optional hook, run right after the S^T MFMAs are issued
+// attend_tile's optional hooks: `mid` runs right after the S^T MFMAs are
+// issued, `vload` fills the V^T operands right before the P.V MFMAs
 struct NoHook {
   __device__ void operator()() const {}
 };
@@ -234,13 +235,13 @@ __device__ __forceinline__ void load_q(typename QTypes<QT>::QOp (&qf)[D / 32], c
 }
 
 // One 16-key tile against one 16-row tile: S^T, online softmax, O^T += V^T P^T.
-template <int D, int QT, bool CAUSAL = false, typename Hook = NoHook>
+template <int D, int QT, bool CAUSAL = false, typename Hook = NoHook, typename VHook = NoHook>
 __device__ __forceinline__ void attend_tile(const Frags<D, QT>& f,
                                             const typename QTypes<QT>::QOp (&qf)[D / 32],
                                             f32x4 (&acc)[D / 16], float& m_run, float& l_run,
                                             float scale_log2, float bias, int nvalid, int g4,
                                             int key0 = 0, RowMask rm = RowMask{false, 0, 0},
-                                            const Hook& mid = Hook{}) {
+                                            const Hook& mid = Hook{}, const VHook& vload = VHook{}) {
   f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kc = 0; kc < D / 32; ++kc) sacc = qk_mfma<QT>(f.kf[kc], qf[kc], sacc);
@@ -291,6 +292,10 @@ __device__ __forceinline__ void attend_tile(const Frags<D, QT>& f,
   l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
   constexpr int PV = QTypes<QT>::PV;
   const u32x2 pB = u32x2{pack2<PV>(pr[0], pr[1]), pack2<PV>(pr[2], pr[3])};
+  if constexpr (!std::is_same<VHook, NoHook>::value) {
+    __builtin_amdgcn_sched_barrier(0);
+    vload();  // V^T operands read only now: fewer registers live across the softmax
+  }
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) acc[j] = mfma_16x16x16<PV>(f.vA[j], pB, acc[j]);
 }
@@ -943,20 +948,26 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
       v_lds[pp] = 16 * G::chunk_pos(t, cv) + 8 * a;
     }
   }
-  auto read_frags = [&](auto sc, Frags<D, QT>& f) {
+  auto read_k = [&](auto sc, Frags<D, QT>& f) {
     const char* st = stage_buf(sc);
     if constexpr (TR) {
 #pragma unroll
       for (int kc = 0; kc < G::NKC; ++kc) f.kf[kc] = *reinterpret_cast<const u32x4*>(st + k_lds[kc]);
-#pragma unroll
-      for (int j = 0; j < VPL; ++j)
-        f.vA[j] = bitcast<u32x2>(__builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(st + v_lds[j])));
     } else {
       u32x4 rk[G::KLD];
 #pragma unroll
       for (int i = 0; i < G::KLD; ++i) rk[i] = *reinterpret_cast<const u32x4*>(st + k_lds[i]);
       k_operands<D, KV, QT>(rk, f);
+    }
+  };
+  auto read_v = [&](auto sc, Frags<D, QT>& f) {
+    const char* st = stage_buf(sc);
+    if constexpr (TR) {
+#pragma unroll
+      for (int j = 0; j < VPL; ++j)
+        f.vA[j] = bitcast<u32x2>(__builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(st + v_lds[j])));
+    } else {
       constexpr int PV = QTypes<QT>::PV;
 #pragma unroll
       for (int pp = 0; pp < VPL / 2; ++pp) {
@@ -970,7 +981,6 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
       }
     }
   };
-
   f32x4 acc[VPL];
   float m_run = kNegInf, l_run = 0.f;
 #pragma unroll
@@ -1036,10 +1046,12 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
     const int key0 = cc.tok0;
     advance(cc);
     Frags<D, QT> f;
-    read_frags(sc, f);
     const bool on = CAUSAL && (key0 + 15 > hi_min || key0 < lo_max);
+    // V^T is read only after the softmax, so it is not live across it: 96
+    // instead of 108 VGPRs for the bf16 block, five waves per SIMD
+    read_k(sc, f);
     attend_tile<D, QT, CAUSAL>(f, qf, acc, m_run, l_run, p.qk_scale_log2, 0.f, nvalid, g4, key0,
-                               RowMask{on, row_hi, row_lo}, refill);
+                               RowMask{on, row_hi, row_lo}, refill, [&]() { read_v(sc, f); });
     return true;
   };
   for (int k = 0;; k += NBUF)
@@ -1063,8 +1075,12 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
 // ---- instantiation table ------------------------------------------------------------
 namespace {
 
-// LDS ring depth of attn_shared_kernel (measured 3 / 4 / 6 / 8 stages: 3 ~ 4 > 6 > 8)
-constexpr int kRingStages = 4;
+// LDS ring depth of attn_shared_kernel.  Three 8 KiB stages let five bf16
+// workgroups share a CU's 160 KiB of LDS (four stages allow only four), and
+// with V read late the kernel fits five waves per SIMD: more waves issuing
+// loads at once (C3 420 -> 407 us, fp8-query block 291 -> 277 us).  Deeper
+// rings measured no faster at equal occupancy (3 ~ 4 ~ 5 > 6 > 8).
+constexpr int kRingStages = 3;
 
 using KernelFn = void (*)(AttnParams);
 
