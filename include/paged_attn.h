@@ -43,8 +43,9 @@
 extern "C" {
 #endif
 
-/* Element types. PA_FP8_E4M3 is the OCP e4m3fn byte format (an fp8 cache is
- * stored as uint8 and viewed as e4m3: flashinfer_ts page, _kv_kernel_dtype). */
+/* Element types.  PA_FP8_E4M3 is the OCP e4m3fn byte format: the pages keep an
+ * fp8 cache in one-byte storage and hand its bytes to the kernel as e4m3
+ * values (flashinfer_ts page, _kv_kernel_dtype). */
 enum pa_dtype { PA_BF16 = 1, PA_FP16 = 2, PA_FP8_E4M3 = 3, PA_F32 = 4 };
 
 enum pa_status {
@@ -195,7 +196,10 @@ int split_kv_combine(const float* part_o, const float* part_lse, int32_t S, int3
  * part_o [N, G, Hq, D] in part_dtype (PA_BF16 | PA_FP16 | PA_F32; dead
  * entries may hold anything: they never reach the result), part_lse
  * [N, G, Hq] fp32, used [N, G] int32,
- * bias [N, G-1] fp32 (may be NULL when G == 1); out [N, Hq, D] in out_dtype;
+ * bias [N, G-1] fp32 (may be NULL when G == 1), each finite or -inf: a
+ * segment whose logit is -inf weighs nothing, and a query with no finite
+ * logit gets out = 0 (the page zeroes the NaN softmax with nan_to_num);
+ * out [N, Hq, D] in out_dtype;
  * lse [N, Hq] (logsumexp of the live part_lse + prior, -inf if none) or NULL. */
 int segment_attn_combine(const void* part_o, int32_t part_dtype, const float* part_lse,
                          const int32_t* used, const float* bias, int32_t N, int32_t G,
@@ -207,7 +211,8 @@ int segment_attn_combine(const void* part_o, int32_t part_dtype, const float* pa
  * 16-bit type as q); per query the rows hold topk remote segments of bs rows
  * and then one local segment of `local` rows.  used [N, topk+1] int32: the
  * number of valid leading rows of each segment (0 = inactive; clamped to the
- * segment's capacity).  bias [N, topk] fp32 (NULL allowed when topk == 0).
+ * segment's capacity).  bias [N, topk] fp32 (NULL allowed when topk == 0),
+ * finite or -inf (a -inf segment weighs nothing, as in segment_attn_combine).
  * Each query attends each segment's valid rows with the given scale (the
  * page uses D**-0.5), then the partial results are merged by
  * segment_attn_combine.  bs and local must be multiples of 8 (PA_EINVAL,

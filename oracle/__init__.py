@@ -7,7 +7,7 @@ it, never links it, and shares no code, tables or constants with it.
 Sources (vLLM API documentation pages):
   * vllm.v1.attention.backends.flashinfer_ts -- uniform query-block paged
     decode over the K/V-halves page, ``_restrict_to_window``, ``forward``
-    scale folding, ``_kv_kernel_dtype`` (fp8 cache viewed as e4m3).
+    scale folding, ``_kv_kernel_dtype`` (fp8 cache bytes read as e4m3).
   * vllm.v1.attention.ops.dash_attention -- ``flash_dash_attention``:
     gathered segments, natural-log LSE, LSE + bias combine.
   * vllm.v1.attention.backends.fa_utils -- ``FlashAttentionCuTeDSLCompileSpec``

@@ -35,7 +35,9 @@ def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
     """O, LSE of softmax(scale * q K^T + key_bias) V for q [R, D], K [n, D], V [n, Dv].
 
     LSE_r = ln sum_j exp(s_rj); O_r = sum_j exp(s_rj - LSE_r) V_j.  With no
-    keys, O = 0 and LSE = -inf.
+    keys, O = 0 and LSE = -inf.  A key whose bias is -inf has weight 0; a row
+    whose every logit is -inf is treated like a row with no keys (the softmax
+    of such a row is NaN, which the DASH combine turns into zero weights).
     """
     q = np.asarray(q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -47,8 +49,11 @@ def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
     if key_bias is not None:
         s = s + np.asarray(key_bias, dtype=np.float64)[None, :]
     m = s.max(axis=1)
-    lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
-    w = np.exp(s - lse[:, None])
+    empty = np.isneginf(m)
+    m_safe = np.where(empty, 0.0, m)
+    tot = np.exp(s - m_safe[:, None]).sum(axis=1)
+    lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, tot)))
+    w = np.where(empty[:, None], 0.0, np.exp(s - np.where(empty, 0.0, lse)[:, None]))
     return w @ V, lse
 
 
@@ -194,6 +199,9 @@ def _weighted_combine(part_o, logits, live):
     part_o [G, ..., D], logits [G, ...], live [G, ...] (bool).
     """
     logits = np.where(live, np.asarray(logits, np.float64), -np.inf)
+    # a live partial with logit -inf (a -inf bias) gets weight 0 like a dead one; if no
+    # finite logit is left the page's softmax is NaN everywhere and nan_to_num makes it 0
+    live = live & (logits > -np.inf)
     m = logits.max(axis=0)
     any_live = live.any(axis=0)
     m_safe = np.where(any_live, m, 0.0)

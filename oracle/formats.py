@@ -3,9 +3,10 @@
 * bf16: the upper 16 bits of an IEEE fp32 word, so decoding is a 16-bit left
   shift into fp32, then widening to fp64 (exact).
 * fp16: IEEE binary16, widened exactly by numpy.
-* e4m3fn: the fp8 format an fp8 KV cache is viewed as (page
-  vllm.v1.attention.backends.flashinfer_ts, ``_kv_kernel_dtype``: a uint8
-  cache is viewed as e4m3; ``_ts_output_dtype`` names torch.float8_e4m3fn).
+* e4m3fn: the fp8 format of an fp8 KV cache (page
+  vllm.v1.attention.backends.flashinfer_ts, ``_kv_kernel_dtype``: one-byte
+  storage whose bytes the kernel reads as e4m3 values; ``_ts_output_dtype``
+  names torch.float8_e4m3fn).
   The table below is built from the format's definition, not from any
   library: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
   exponent field 0 is subnormal (m/8 * 2^-6); there are no infinities and

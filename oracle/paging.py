@@ -13,11 +13,12 @@ def window_start_page(L: int, window: int, query_len: int, page_size: int) -> in
     """First page a page-aligned sliding window can reach.
 
     Page vllm.v1.attention.backends.flashinfer_ts, module docstring
-    "Sliding window" and ``_restrict_to_window``: the query block ends the
-    sequence, so a symmetric window around it is the suffix that starts
-    ``window + query_len - 1`` tokens before the end; that start is rounded
-    DOWN to a page (floor division, clamped at page 0).  ``window <= 0``
-    means no window (every key visible).
+    "Sliding window" and ``_restrict_to_window``.  Every query token of the
+    block sits at the end of its request, so the keys any of them can reach
+    through a window of ``window`` keys begin ``window + query_len - 1`` keys
+    before the end of the sequence.  The start page is that key index
+    divided by the page size with the floor taken, never below page 0.
+    ``window <= 0`` means no window (every key visible).
     """
     if window <= 0:
         return 0

@@ -107,10 +107,15 @@ def new_workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(((max(int(nbytes), 16) + 15) // 16) * 16, dtype=torch.uint8, device=device)
 
 
-def _check_paged_inputs(q, block_table, seq_lens):
+def _check_paged_inputs(q, k, v, block_table, seq_lens):
     if q.dim() != 4:
         raise ValueError("q must be [B, query_len, Hq, D]")
     _need(q, "q")
+    # the kernels step through K and V rows by the token stride and read D values of
+    # each; a view narrower than q's head_dim would run into the next row or past the pool
+    if k.dim() != 4 or v.dim() != 4 or k.shape[3] != q.shape[3] or v.shape[3] != q.shape[3]:
+        raise ValueError(f"k and v must be [pages, Hkv, page_size, D] views with q's head_dim "
+                         f"D={q.shape[3]} (got k {tuple(k.shape)}, v {tuple(v.shape)})")
     B = q.shape[0]
     if block_table.dim() != 2 or block_table.shape[0] != B or block_table.stride(1) != 1:
         raise ValueError("block_table must be [B, W] with unit column stride")
@@ -130,7 +135,7 @@ def paged_attn_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_tabl
     (paged_attn_run_causal); otherwise the dense block with the page-aligned window.
     Returns (out [B, sq, Hq, D], lse [B, sq, Hq] fp32 natural log, or None)."""
     B, sq, Hq, D = q.shape
-    _check_paged_inputs(q, block_table, seq_lens)
+    _check_paged_inputs(q, k, v, block_table, seq_lens)
     desc = kv_desc(k, v, k_scale=k_scale, v_scale=v_scale)
     if out is None:
         default = q.dtype if q.dtype in (torch.bfloat16, torch.float16) else torch.bfloat16
@@ -167,7 +172,7 @@ def paged_attn_partial(q, k, v, block_table, seq_lens, *, scale: float, num_spli
                        part_o: Optional[torch.Tensor] = None, part_lse: Optional[torch.Tensor] = None):
     """Split-KV partials: (part_o [S, B*sq, Hq, D] fp32, part_lse [S, B*sq, Hq] fp32)."""
     B, sq, Hq, D = q.shape
-    _check_paged_inputs(q, block_table, seq_lens)
+    _check_paged_inputs(q, k, v, block_table, seq_lens)
     desc = kv_desc(k, v, k_scale=k_scale, v_scale=v_scale)
     W = block_table.shape[1]
     S = resolve_splits(B, sq, Hq, desc.num_kv_heads, D, desc.page_size, W, window, num_splits)

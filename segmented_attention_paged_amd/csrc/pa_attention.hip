@@ -235,7 +235,11 @@ __device__ __forceinline__ void load_q(typename QTypes<QT>::QOp (&qf)[D / 32], c
 }
 
 // One 16-key tile against one 16-row tile: S^T, online softmax, O^T += V^T P^T.
-template <int D, int QT, bool CAUSAL = false, typename Hook = NoHook, typename VHook = NoHook>
+// EMPTY_ROWS: a row may have seen only -inf logits so far (causal rows before
+// their first key; fused segments whose bias is -inf), so its running max can
+// still be -inf and the exponent reference must stay finite.
+template <int D, int QT, bool CAUSAL = false, bool EMPTY_ROWS = CAUSAL, typename Hook = NoHook,
+          typename VHook = NoHook>
 __device__ __forceinline__ void attend_tile(const Frags<D, QT>& f,
                                             const typename QTypes<QT>::QOp (&qf)[D / 32],
                                             f32x4 (&acc)[D / 16], float& m_run, float& l_run,
@@ -276,16 +280,16 @@ __device__ __forceinline__ void attend_tile(const Frags<D, QT>& f,
   if (__ballot(tmax > m_run + kRescaleSlack) != 0) {
     const float m_new = fmaxf(m_run, tmax);
     float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile (m_run = -inf)
-    // causal: a row that has seen no key yet (m_new = -inf) keeps its zeros
-    if constexpr (CAUSAL) alpha = m_new == kNegInf ? 1.f : alpha;
+    // a row that has seen no finite logit yet (m_new = -inf) keeps its zeros
+    if constexpr (EMPTY_ROWS) alpha = m_new == kNegInf ? 1.f : alpha;
     l_run *= alpha;
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) acc[j] *= alpha;
     m_run = m_new;
   }
-  // causal rows with no key so far have only -inf logits: any finite reference
+  // rows with no finite logit so far have only -inf logits: any finite reference
   float m_ref = m_run;
-  if constexpr (CAUSAL) m_ref = m_run == kNegInf ? 0.f : m_run;
+  if constexpr (EMPTY_ROWS) m_ref = m_run == kNegInf ? 0.f : m_run;
   float pr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s[i] - m_ref);
@@ -656,9 +660,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
     const bool on = CAUSAL && (ti.key0 + 15 > hi_min || ti.key0 < lo_max);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
-      attend_tile<D, QT, CAUSAL>(f, qf[rt], acc[rt], m_run[rt], l_run[rt], p.qk_scale_log2,
-                                 ti.bias, ti.nvalid, g4, ti.key0,
-                                 RowMask{on, row_hi[rt], row_lo[rt]});
+      attend_tile<D, QT, CAUSAL, CAUSAL || MODE == MODE_SEGMENT_FUSED>(
+          f, qf[rt], acc[rt], m_run[rt], l_run[rt], p.qk_scale_log2, ti.bias, ti.nvalid, g4,
+          ti.key0, RowMask{on, row_hi[rt], row_lo[rt]});
   };
 
   // main loop: tile k+1 is in flight while tile k is computed

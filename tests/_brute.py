@@ -17,7 +17,15 @@ def bf16_bits_to_float(bits: int) -> float:
 
 
 def brute_attention_row(q, keys, values, scale, key_bias=None):
-    """softmax(scale * q.k_j + bias_j) weighted sum of values; returns (out list, lse)."""
+    """softmax(scale * q.k_j + bias_j) weighted sum of values; returns (out list, lse).
+
+    A key with bias -inf has weight e^-inf = 0 and is left out; with no key left
+    the result is (zeros, -inf)."""
+    if key_bias is not None:
+        kept = [j for j in range(len(keys)) if key_bias[j] != -math.inf]
+        keys = [keys[j] for j in kept]
+        values = [values[j] for j in kept]
+        key_bias = [key_bias[j] for j in kept]
     n = len(keys)
     if n == 0:
         return [0.0] * (len(values[0]) if values else len(q)), -math.inf

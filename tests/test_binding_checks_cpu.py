@@ -43,6 +43,19 @@ def test_paged_run_shape_dtype_and_device_errors():
         sap.paged_attn_run(q, k, v, bt, lens, scale=0.1)
 
 
+def test_kv_views_must_carry_the_query_head_dim():
+    # a [pages, Hkv, P, 2*64] cache split into 64-wide halves, read with a D=128 query:
+    # each V read would run into the next token's K and past the pool's last slot
+    q = torch.zeros((2, 1, 4, 128), dtype=torch.bfloat16)
+    _, k, v, bt, lens = _paged(sq=1, D=64)
+    with pytest.raises(ValueError, match="head_dim"):
+        sap.paged_attn_run(q, k, v, bt, lens, scale=0.1)
+    with pytest.raises(ValueError, match="head_dim"):
+        sap.paged_attn_partial(q, k, v, bt, lens, scale=0.1, num_splits=2)
+    with pytest.raises(ValueError, match="head_dim"):
+        sap.paged_attn_run(q[..., :64].contiguous(), k, v[..., :32], bt, lens, scale=0.1)
+
+
 def test_partial_and_combine_buffer_errors():
     q, k, v, bt, lens = _paged()
     with pytest.raises(ValueError, match="part_o must have shape"):

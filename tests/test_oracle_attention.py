@@ -408,6 +408,49 @@ def test_all_dead_query_is_zero():
     assert np.all(O[2] == 0) and np.all(np.isneginf(L[2]))
 
 
+def test_minus_inf_bias_weighs_nothing():
+    # The page's combine takes a softmax over LSE + bias and then nan_to_num: a live
+    # segment whose bias is -inf gets weight e^-inf = 0, exactly like a dead one, and a
+    # query whose every live logit is -inf gets the NaN softmax zeroed, i.e. output 0.
+    s = _seg(poison=False, zero_frac=0.0)
+    q, k, v, used, bias = _seg_np(s)
+    b2 = bias.copy()
+    b2[1, 2] = -np.inf           # one remote segment of query 1
+    b2[4, :] = -np.inf           # every remote segment of query 4 (the local one is live)
+    b2[0, :] = -np.inf           # query 0: every remote segment, and its local one is dead
+    u2 = used.copy()
+    u2[0, s.topk] = 0
+    O, L = _seg_run(s, q, k, v, u2, b2)
+    ref_used = u2.copy()
+    ref_used[1, 2] = 0
+    ref_used[4, :s.topk] = 0
+    ref_used[0, :] = 0
+    Or, Lr = _seg_run(s, q, k, v, ref_used, bias)
+    np.testing.assert_allclose(O, Or, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(L[1:], Lr[1:], rtol=0, atol=1e-14)
+    assert np.all(O[0] == 0) and np.all(np.isneginf(L[0]))
+    Ou, Lu = oracle.segment_attention_union(q, k, v, u2, b2, topk=s.topk, bs=s.bs,
+                                            local=s.local, scale=s.scale)
+    np.testing.assert_allclose(Ou, O, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(Lu, L, rtol=0, atol=1e-12)
+    # brute force over the union of live prefixes for the three queries touched
+    per = s.topk * s.bs + s.local
+    for n in (0, 1, 4):
+        for h in range(s.Hq):
+            kvh = h // 2
+            keys, vals, kb = [], [], []
+            for g in range(s.topk + 1):
+                base = n * per + (g * s.bs if g < s.topk else s.topk * s.bs)
+                for j in range(int(u2[n, g])):
+                    keys.append([bf16_bits_to_float(x) for x in k[base + j, kvh]])
+                    vals.append([bf16_bits_to_float(x) for x in v[base + j, kvh]])
+                    kb.append(float(b2[n, g]) if g < s.topk else 0.0)
+            qrow = [bf16_bits_to_float(x) for x in q[n, h]]
+            out, lse = brute_attention_row(qrow, keys, vals, s.scale, kb)
+            np.testing.assert_allclose(O[n, h], out, rtol=0, atol=1e-12)
+            assert (math.isinf(lse) and np.isneginf(L[n, h])) or L[n, h] == pytest.approx(lse, abs=1e-12)
+
+
 def test_full_segments_zero_bias_is_plain_attention():
     s = _seg(N=2, poison=False, zero_frac=0.0)
     q, k, v, used, bias = _seg_np(s)

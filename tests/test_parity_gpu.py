@@ -302,6 +302,28 @@ def test_segment_attention(sap, name, fused):
     compare(out, lse, O, L, TOL_BF16, what=f"{name} fused={fused}")
 
 
+@pytest.mark.parametrize("fused", [True, False])
+def test_segment_minus_inf_bias(sap, fused):
+    # a live segment with bias -inf weighs nothing; a query whose live logits are all
+    # -inf ends as out = 0, lse = -inf (the page's nan_to_num of a NaN softmax)
+    s = make_segments(seed=19, poison=True, zero_frac=0.0, name="ninf", **SEG["seg_small"])
+    bias = s.bias.clone()
+    used = s.used.clone()
+    bias[0, :] = float("-inf")
+    used[0, s.topk] = 0          # query 0: nothing finite left
+    bias[1, 0] = float("-inf")   # query 1: its first segment (a wave's first tile)
+    bias[4, :] = float("-inf")   # query 4: only the local segment counts
+    s.bias, s.used = bias, used
+    O, L = oracle.segment_attention(to_numpy_bits(s.q), to_numpy_bits(s.k), to_numpy_bits(s.v),
+                                    used.numpy(), bias.numpy(), topk=s.topk, bs=s.bs,
+                                    local=s.local, scale=s.scale)
+    d = s.to(DEV)
+    out, lse = sap.segment_attn_run(d.q, d.k, d.v, d.used, d.bias, bs=s.bs, local=s.local,
+                                    fused=fused)
+    compare(out, lse, O, L, TOL_BF16, what=f"-inf bias fused={fused}")
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
 # ---- integer plan on the device --------------------------------------------------
 @pytest.mark.parametrize("name", ["decode_d128_g4", "block_sq16_window", "page24_window"])
 @pytest.mark.parametrize("splits", [1, 3, 0, -2])
