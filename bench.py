@@ -16,7 +16,13 @@ The "kv_write" entry times paged_kv_write (new K/V rows scattered into the
 page cache, bf16 and fp8) for a 65536-token prefill chunk and a 64-token
 decode step; its bytes are the rows read plus the slot rows written.
 
-    python bench.py [--steps K] [--warmup W] [--all] [--no-cpu-baseline] [--no-kv-write]
+Every other configuration (the tiny decode, the windowed and causal sq=16 blocks, the
+fp8-query block, long-context Split-KV in bf16 and fp8, the DASH segments fused and
+two-stage) is timed after the headline in the same run, each with the fp64 oracle
+timed beside it on the host over a bounded sample ("workloads" in the JSON line).
+
+    python bench.py [--steps K] [--warmup W] [--headline-only] [--no-cpu-baseline]
+                    [--no-kv-write] [--cpu-seconds S] [--cpu-seconds-other S]
 """
 
 from __future__ import annotations
@@ -101,13 +107,14 @@ def time_events(fn, steps: int, warmup: int, flush=None):
 _FLUSH = {}
 
 
-def mall_flush(nbytes: int):
-    """A 512 MB read run between timed calls when a call touches less than 1 GiB, so its
-    data is not served from the 256 MB Infinity Cache; None otherwise.  A read, not a
-    fill: a fill leaves dirty lines whose write-back the timed call would pay for."""
+def mall_flush(nbytes: int, force: bool = False):
+    """A 512 MB read run between timed calls when a call touches less than 1 GiB (or
+    always, with force), so its data is not served from the 256 MB Infinity Cache; None
+    otherwise.  A read, not a fill: a fill leaves dirty lines whose write-back the timed
+    call would pay for."""
     import torch
 
-    if nbytes >= (1 << 30):
+    if nbytes >= (1 << 30) and not force:
         return None
     if "buf" not in _FLUSH:
         _FLUSH["buf"] = torch.ones(1 << 26, dtype=torch.int64, device="cuda")
@@ -146,7 +153,8 @@ class PagedBench:
         lens, _, _ = sap.paged_attn_describe_host(
             inp.block_table.cpu(), inp.seq_lens.cpu(), query_len=inp.sq, Hq=inp.Hq, Hkv=inp.Hkv,
             D=inp.D, page_size=inp.P, window=inp.window, num_splits=1)
-        self.visible = int(lens.to(torch.int64).sum())
+        self.visible_lens = [int(x) for x in lens.tolist()]
+        self.visible = sum(self.visible_lens)
         elem = 1 if inp.kv_dtype == "fp8_e4m3" else 2
         self.kv_bytes = self.visible * inp.Hkv * 2 * inp.D * elem
         self.flops = 4 * inp.sq * inp.Hq * inp.D * self.visible
@@ -168,9 +176,19 @@ class PagedBench:
                                     part_lse=self.part_lse)
 
 
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        return int(max([d.get("num_threads", 1) for d in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def cpu_baseline(pb: PagedBench, seconds: float):
     """The fp64 oracle on the host over the same workload: requests in order,
-    wrapping around for further passes, until `seconds` of oracle time."""
+    wrapping around for further passes, until `seconds` of oracle time (at least
+    one request).  Each request is evaluated from host copies of its own pages."""
     import numpy as np
     import torch
 
@@ -182,17 +200,15 @@ def cpu_baseline(pb: PagedBench, seconds: float):
     bt = inp.block_table.cpu()
     lens = inp.seq_lens.cpu()
     q = to_numpy_bits(inp.q.cpu())
-    try:
-        from threadpoolctl import threadpool_info
-
-        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = 1
+    q_dtype = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.uint8: "fp8_e4m3"}[inp.q.dtype]
+    elem = 1 if inp.kv_dtype == "fp8_e4m3" else 2
     host = {}  # request -> (k, v, table): host copies of exactly its pages
     done, toks, t_used = 0, 0, 0.0
-    while t_used < seconds:
+    while t_used < seconds or done == 0:
         b = done % inp.B
         if b not in host:
+            if len(host) > 4:
+                host.clear()
             n = -(-int(lens[b]) // inp.P)
             pages = bt[b, :n].to(torch.long)
             cache = to_numpy_bits(inp.cache.index_select(0, pages.to(inp.cache.device)).cpu())
@@ -202,22 +218,57 @@ def cpu_baseline(pb: PagedBench, seconds: float):
             host[b] = (k, v, table)
         k, v, table = host[b]
         t0 = time.perf_counter()
-        oracle.paged_attention(q, "bf16", k, v, inp.kv_dtype, table, lens.numpy(), scale=inp.scale,
-                               window=inp.window, k_scale=inp.k_scale, v_scale=inp.v_scale,
-                               requests=[b])
+        oracle.paged_attention(q, q_dtype, k, v, inp.kv_dtype, table, lens.numpy(),
+                               scale=inp.scale, q_scale=inp.q_scale, window=inp.window,
+                               k_scale=inp.k_scale, v_scale=inp.v_scale, requests=[b],
+                               causal=pb.causal)
         t_used += time.perf_counter() - t0
         done += 1
-        toks += int(lens[b])
+        toks += int(pb.visible_lens[b])
     return {
         "value": done * inp.sq / t_used,
         "unit": "tokens/s",
-        "cores": int(blas_threads),
+        "cores": _blas_threads(),
         "kind": "oracle",
-        "sample": f"{done} request evaluations of {pb.name} ({done / inp.B:.1f} passes over its "
-                  f"{inp.B} requests, all {inp.Hkv} kv heads, {toks} keys), fp64 numpy, "
-                  f"{t_used:.1f} s",
+        "sample": f"{done} request evaluations of {pb.name}{' (causal)' if pb.causal else ''} "
+                  f"({done / inp.B:.2f} passes over its {inp.B} requests, all {inp.Hkv} kv heads, "
+                  f"{toks} visible keys), fp64 numpy, {t_used:.1f} s",
         "host_cpus": len(os.sched_getaffinity(0)),
-        "kv_gbps_equiv": toks * inp.Hkv * 2 * inp.D * 2 / t_used / 1e9,
+        "kv_gbps_equiv": toks * inp.Hkv * 2 * inp.D * elem / t_used / 1e9,
+    }
+
+
+def cpu_baseline_segments(s, seconds: float):
+    """The fp64 oracle (two-stage form) on the host, one DASH query at a time (each
+    query's own rows of K/V), until `seconds` of oracle time."""
+    import oracle
+    from workloads import to_numpy_bits
+
+    q = to_numpy_bits(s.q.cpu())
+    k = to_numpy_bits(s.k.cpu())
+    v = to_numpy_bits(s.v.cpu())
+    used = s.used.cpu().numpy()
+    bias = s.bias.cpu().numpy()
+    per = s.topk * s.bs + s.local
+    done, toks, t_used = 0, 0, 0.0
+    while t_used < seconds or done == 0:
+        n = done % s.N
+        rows = slice(n * per, (n + 1) * per)
+        t0 = time.perf_counter()
+        oracle.segment_attention(q[n:n + 1], k[rows], v[rows], used[n:n + 1], bias[n:n + 1],
+                                 topk=s.topk, bs=s.bs, local=s.local, scale=s.scale)
+        t_used += time.perf_counter() - t0
+        done += 1
+        toks += int(used[n].sum())
+    return {
+        "value": done / t_used,
+        "unit": "queries/s",
+        "cores": _blas_threads(),
+        "kind": "oracle",
+        "sample": f"{done} of the {s.N} DASH queries (all {s.topk + 1} segments and {s.Hkv} kv "
+                  f"heads each, {toks} valid rows), fp64 numpy two-stage form, {t_used:.1f} s",
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "kv_gbps_equiv": toks * s.Hkv * 2 * s.D * 2 / t_used / 1e9,
     }
 
 
@@ -233,7 +284,44 @@ def calibrate_copy(n_bytes: int = 1 << 30, reps: int = 3):
     log(f"calibration copy: {reps} x {n_bytes} bytes read and written")
 
 
-def run_segments(steps, warmup):
+def measure_paged(name: str, causal: bool, steps: int, warmup: int, cpu_seconds: float,
+                  pb: PagedBench = None):
+    """Step time (paged_attn_run, combine included), the attention kernel alone (the
+    partial pass in the same launch configuration; dense blocks only, the partial entry
+    point has no causal form) and the oracle beside it, for one paged workload."""
+    import torch
+
+    pb = pb or PagedBench(name, causal=causal)
+    inp = pb.inp
+    flush = mall_flush(pb.kv_bytes)
+    step_ms, _ = time_events(pb.step, steps, warmup, flush)
+    res = {
+        "workload": name, "causal": causal, "B": inp.B, "query_len": inp.sq, "Hq": inp.Hq,
+        "Hkv": inp.Hkv, "head_dim": inp.D, "kv_dtype": inp.kv_dtype,
+        "q_dtype": str(inp.q.dtype).replace("torch.", ""), "window": inp.window,
+        "splits": pb.plan["splits"], "grid": pb.plan["grid"], "visible_keys": pb.visible,
+        "kv_bytes": pb.kv_bytes, "mall_flush": flush is not None,
+        "step_us": step_ms * 1e3, "tokens_per_s": inp.B * inp.sq / (step_ms / 1e3),
+        "kv_gbps": pb.kv_bytes / step_ms / 1e6, "hbm_frac": pb.kv_bytes / step_ms / 1e6 / HBM_PEAK_GBPS,
+    }
+    if not causal:
+        kern_ms, _ = time_events(pb.kernel, steps, warmup, flush)
+        res.update(kernel_us=kern_ms * 1e3, kernel_gbps=pb.kv_bytes / kern_ms / 1e6,
+                   kernel_hbm_frac=pb.kv_bytes / kern_ms / 1e6 / HBM_PEAK_GBPS)
+    if inp.sq >= 16:
+        res.update(mfma_tflops=pb.flops / step_ms / 1e9,
+                   mfma_frac_of_bf16_peak=pb.flops / step_ms / 1e9 / BF16_DENSE_TFLOPS)
+    log(f"{name}{' causal' if causal else ''}: step {step_ms * 1e3:.1f} us "
+        f"({res['kv_gbps']:.0f} GB/s)" + (f", kernel {res['kernel_us']:.1f} us" if not causal else ""))
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(pb, cpu_seconds)
+    del pb
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_segments(steps, warmup, cpu_seconds):
+    """C5: the fused kernel (one launch) and the two-stage form (partials + combine)."""
     import torch
 
     import segmented_attention_paged_amd as sap
@@ -244,15 +332,21 @@ def run_segments(steps, warmup):
     ws = torch.empty(sap.segment_attn_workspace_size(s.N, s.topk, s.Hq, s.D), dtype=torch.uint8,
                      device="cuda")
     kv_bytes = int(s.used.to(torch.int64).sum()) * s.Hkv * 2 * s.D * 2
-    res = {}
+    res = {"workload": "c5_dash_segments", "N": s.N, "Hq": s.Hq, "Hkv": s.Hkv, "head_dim": s.D,
+           "topk": s.topk, "bs": s.bs, "local": s.local, "kv_bytes": kv_bytes, "mall_flush": True}
     for fused in (True, False):
         fn = lambda: sap.segment_attn_run(s.q, s.k, s.v, s.used, s.bias, bs=s.bs, local=s.local,
                                           fused=fused, out=out, workspace=ws)
         ms, _ = time_events(fn, steps, warmup, mall_flush(kv_bytes))
         res["fused" if fused else "two_stage"] = {
-            "us": ms * 1e3, "kv_gbps": kv_bytes / ms / 1e6,
+            "step_us": ms * 1e3, "queries_per_s": s.N / (ms / 1e3), "kv_gbps": kv_bytes / ms / 1e6,
             "hbm_frac": kv_bytes / ms / 1e6 / HBM_PEAK_GBPS}
-    res["kv_bytes"] = kv_bytes
+        log(f"c5_dash_segments {'fused' if fused else 'two-stage'}: {ms * 1e3:.1f} us "
+            f"({kv_bytes / ms / 1e6:.0f} GB/s)")
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline_segments(s, cpu_seconds)
+    del s, out, ws
+    torch.cuda.empty_cache()
     return res
 
 
@@ -284,6 +378,15 @@ def run_kv_write(steps, warmup):
     return res
 
 
+# Every other configuration, measured in the default run after the headline:
+# (workload, causal).  C3 (dense) is measured with the headline's sq=16 block.
+OTHER_PAGED = [
+    ("c1_tiny", False), ("c3w_query_block_window", False), ("c3_query_block", True),
+    ("c3w_query_block_window", True), ("c3f_query_block_fp8", False), ("c4_split_kv", False),
+    ("c4f_split_kv_fp8", False),
+]
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,11 +395,14 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="c2_gqa_decode")
     ap.add_argument("--num-splits", type=int, default=None,
                     help="override the split policy (0 auto, S > 0, -c chunks of c pages)")
-    ap.add_argument("--all", action="store_true", help="also time every other workload")
-    ap.add_argument("--no-block", action="store_true", help="skip the sq=16 MFMA measurement")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the headline workload (no sq=16 block, other configs or cache write)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kv-write", action="store_true", help="skip the cache-write measurement")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle seconds for the headline workload's CPU baseline")
+    ap.add_argument("--cpu-seconds-other", type=float, default=2.0,
+                    help="oracle seconds for each other configuration's CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args(argv)
 
@@ -316,6 +422,9 @@ def main(argv=None) -> int:
     sap.load()
     if args.calibrate_copy:
         calibrate_copy()
+    cpu_s = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    cpu_o = 0.0 if args.no_cpu_baseline else args.cpu_seconds_other
+    sub_steps, sub_warm = max(10, args.steps // 2), max(3, args.warmup // 2)
 
     pb = PagedBench(args.workload, args.num_splits)
     inp = pb.inp
@@ -325,11 +434,20 @@ def main(argv=None) -> int:
     kern_ms, _ = time_events(pb.kernel, args.steps, args.warmup)
     log(f"step {step_ms * 1e3:.1f} us (wall {step_wall * 1e3:.1f} us), attention kernel "
         f"{kern_ms * 1e3:.1f} us")
+    # the same step with a 512 MB read between calls: what the Infinity Cache holds of
+    # the last call does not count
+    flushed_ms, _ = time_events(pb.step, sub_steps, sub_warm, mall_flush(pb.kv_bytes, force=True))
+    log(f"step after a 512 MB read flush: {flushed_ms * 1e3:.1f} us")
     tok_s = inp.B * inp.sq / (step_ms / 1e3)
     kv_gbps = pb.kv_bytes / step_ms / 1e6
     kern_gbps = pb.kv_bytes / kern_ms / 1e6
     traffic = read_counters(args.workload)
-
+    headline_cfg = {
+        "workload": args.workload, "B": inp.B, "query_len": inp.sq, "Hq": inp.Hq,
+        "Hkv": inp.Hkv, "head_dim": inp.D, "page_size": inp.P, "window": inp.window,
+        "visible_keys": pb.visible, "splits": pb.plan["splits"],
+        "chunk_pages": pb.plan["chunk_pages"], "grid": pb.plan["grid"],
+    }
     result = {
         "metric": METRIC,
         "value": tok_s,
@@ -343,14 +461,10 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": "bf16" if inp.kv_dtype == "bf16" else "fp8_e4m3 kv, bf16 q",
         "data": "synthetic",
-        "config": {
-            "workload": args.workload, "B": inp.B, "query_len": inp.sq, "Hq": inp.Hq,
-            "Hkv": inp.Hkv, "head_dim": inp.D, "page_size": inp.P, "window": inp.window,
-            "visible_keys": pb.visible, "splits": pb.plan["splits"],
-            "chunk_pages": pb.plan["chunk_pages"], "grid": pb.plan["grid"],
-        },
+        "config": headline_cfg,
         "kv_gbps": kv_gbps,
         "hbm_frac": kv_gbps / HBM_PEAK_GBPS,
+        "step_us_after_mall_flush": flushed_ms * 1e3,
         "roofline": {
             "kernel": "attn_kernel (paged partial pass)",
             "bound": "hbm",
@@ -363,72 +477,33 @@ def main(argv=None) -> int:
             "algorithmic_bytes_per_launch": pb.kv_bytes,
         },
     }
+    workloads = {args.workload: dict(headline_cfg, step_us=step_ms * 1e3, tokens_per_s=tok_s,
+                                     kv_gbps=kv_gbps, hbm_frac=kv_gbps / HBM_PEAK_GBPS,
+                                     kernel_us=kern_ms * 1e3, kernel_gbps=kern_gbps,
+                                     kernel_hbm_frac=kern_gbps / HBM_PEAK_GBPS,
+                                     step_us_after_mall_flush=flushed_ms * 1e3)}
+    if cpu_s > 0:
+        result["cpu_baseline"] = cpu_baseline(pb, cpu_s)
+        workloads[args.workload]["cpu_baseline"] = result["cpu_baseline"]
     del pb
     torch.cuda.empty_cache()
 
-    if not args.no_block:
-        bb = PagedBench("c3_query_block")
-        ms, _ = time_events(bb.step, max(10, args.steps // 2), max(3, args.warmup // 2))
+    if not args.headline_only:
+        c3 = measure_paged("c3_query_block", False, sub_steps, sub_warm, cpu_o)
+        workloads["c3_query_block"] = c3
         result["sq16_block"] = {
-            "workload": "c3_query_block", "us": ms * 1e3,
-            "tokens_per_s": bb.inp.B * bb.inp.sq / (ms / 1e3),
-            "kv_gbps": bb.kv_bytes / ms / 1e6, "hbm_frac": bb.kv_bytes / ms / 1e6 / HBM_PEAK_GBPS,
-            "mfma_tflops": bb.flops / ms / 1e9,
-            "mfma_frac_of_bf16_peak": bb.flops / ms / 1e9 / BF16_DENSE_TFLOPS,
-            "splits": bb.plan["splits"],
+            "workload": "c3_query_block", "us": c3["step_us"], "tokens_per_s": c3["tokens_per_s"],
+            "kv_gbps": c3["kv_gbps"], "hbm_frac": c3["hbm_frac"], "mfma_tflops": c3["mfma_tflops"],
+            "mfma_frac_of_bf16_peak": c3["mfma_frac_of_bf16_peak"], "splits": c3["splits"],
+            "kernel_us": c3["kernel_us"], "kernel_hbm_frac": c3["kernel_hbm_frac"],
         }
-        log(f"c3_query_block: {ms * 1e3:.1f} us, MFMA {bb.flops / ms / 1e9:.1f} TFLOP/s")
-        del bb
-        torch.cuda.empty_cache()
-        # the same blocks with the causal mask (exact per-token window for C3w); the
-        # pages read are the same as the dense block's, so the byte count is too
-        causal = {}
-        for name in ("c3_query_block", "c3w_query_block_window"):
-            bb = PagedBench(name, causal=True)
-            ms, _ = time_events(bb.step, max(10, args.steps // 2), max(3, args.warmup // 2),
-                                mall_flush(bb.kv_bytes))
-            causal[name] = {"us": ms * 1e3, "tokens_per_s": bb.inp.B * bb.inp.sq / (ms / 1e3),
-                            "kv_gbps": bb.kv_bytes / ms / 1e6,
-                            "hbm_frac": bb.kv_bytes / ms / 1e6 / HBM_PEAK_GBPS,
-                            "splits": bb.plan["splits"]}
-            log(f"{name} causal: {ms * 1e3:.1f} us")
-            del bb
-            torch.cuda.empty_cache()
-        result["sq16_block"]["causal"] = causal
-        # fp8 query against an fp8 cache (q.k on fp8 MFMA, P.V in bf16)
-        bb = PagedBench("c3f_query_block_fp8")
-        ms, _ = time_events(bb.step, max(10, args.steps // 2), max(3, args.warmup // 2))
-        result["sq16_block"]["fp8_query"] = {
-            "workload": "c3f_query_block_fp8", "us": ms * 1e3,
-            "tokens_per_s": bb.inp.B * bb.inp.sq / (ms / 1e3), "kv_gbps": bb.kv_bytes / ms / 1e6,
-            "hbm_frac": bb.kv_bytes / ms / 1e6 / HBM_PEAK_GBPS, "splits": bb.plan["splits"]}
-        log(f"c3f_query_block_fp8: {ms * 1e3:.1f} us, {bb.kv_bytes / ms / 1e6:.0f} GB/s")
-        del bb
-        torch.cuda.empty_cache()
-
-    if not args.no_kv_write:
-        result["kv_write"] = run_kv_write(max(10, args.steps // 2), max(3, args.warmup // 2))
-
-    if args.all:
-        extra = {}
-        for name in ["c1_tiny", "c3w_query_block_window", "c4_split_kv", "c4f_split_kv_fp8"]:
-            bb = PagedBench(name)
-            flush = mall_flush(bb.kv_bytes)
-            ms, _ = time_events(bb.step, max(10, args.steps // 2), max(3, args.warmup // 2), flush)
-            extra[name] = {"us": ms * 1e3, "tokens_per_s": bb.inp.B * bb.inp.sq / (ms / 1e3),
-                           "kv_gbps": bb.kv_bytes / ms / 1e6,
-                           "hbm_frac": bb.kv_bytes / ms / 1e6 / HBM_PEAK_GBPS,
-                           "splits": bb.plan["splits"]}
-            log(f"{name}: {ms * 1e3:.1f} us, {bb.kv_bytes / ms / 1e6:.0f} GB/s")
-            del bb
-            torch.cuda.empty_cache()
-        extra["c5_dash_segments"] = run_segments(max(10, args.steps // 2), max(3, args.warmup // 2))
-        result["other_workloads"] = extra
-
-    if not args.no_cpu_baseline:
-        pb2 = PagedBench(args.workload, args.num_splits)
-        result["cpu_baseline"] = cpu_baseline(pb2, args.cpu_seconds)
-        del pb2
+        for name, causal in OTHER_PAGED:
+            key = name + ("_causal" if causal else "")
+            workloads[key] = measure_paged(name, causal, sub_steps, sub_warm, cpu_o)
+        workloads["c5_dash_segments"] = run_segments(sub_steps, sub_warm, cpu_o)
+        if not args.no_kv_write:
+            result["kv_write"] = run_kv_write(sub_steps, sub_warm)
+    result["workloads"] = workloads
 
     print(json.dumps(result), flush=True)
     return 0
