@@ -129,6 +129,29 @@ int paged_attn_run(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
                    void* out, int32_t out_dtype, float* lse,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of the device scratch paged_attn_run_noalloc keeps per GPU (96 MiB:
+ * the Split-KV partials of a 32 x 16-token block of 32 heads at D = 128 in
+ * 8 splits take 64.5 MiB). */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+
+/* paged_attn_run without a workspace argument, for callers that cannot
+ * allocate device memory (code under hipGraph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, plan, kernels and results
+ * as paged_attn_run; the Split-KV partials go to a static device array of
+ * PA_NOALLOC_SCRATCH_BYTES that each GPU holds until the process ends.  The
+ * call allocates and frees nothing.  Its first call on a device looks the
+ * array's address up (hipGetSymbolAddress) for the device `stream` belongs
+ * to.  A shape whose partials exceed the array (paged_attn_workspace_size >
+ * PA_NOALLOC_SCRATCH_BYTES) returns PA_EWORKSPACE before anything is
+ * enqueued.  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (other streams, other threads) race and give
+ * wrong results.  Nothing in the array needs clearing between calls. */
+int paged_attn_run_noalloc(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
+                           const int32_t* block_table, int64_t bt_row_stride, int32_t bt_width,
+                           const int32_t* seq_lens, int32_t B, int32_t query_len, int32_t Hq,
+                           int32_t D, float scale, int32_t window, int32_t num_splits,
+                           void* out, int32_t out_dtype, float* lse, hipStream_t stream);
+
 /* Causal query block (flashinfer_ts _get_plan: mask_type "causal" with
  * window_left = window - 1).  Arguments, plan, splits and workspace as
  * paged_attn_run; only the mask differs.  Token t of request b sits at

@@ -22,6 +22,7 @@ from .api import (  # noqa: F401
     paged_attn_partial,
     paged_attn_run,
     paged_attn_run_causal,
+    paged_attn_run_noalloc,
     paged_kv_write,
     plan,
     resolve_splits,

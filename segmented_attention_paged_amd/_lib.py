@@ -48,6 +48,8 @@ _kvp = ctypes.POINTER(PaKvDesc)
 SIGNATURES = {
     "paged_attn_run": (ctypes.c_int, [_vp, _i32, _kvp, _vp, _i64, _i32, _vp, _i32, _i32, _i32, _i32,
                                       _f32, _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "paged_attn_run_noalloc": (ctypes.c_int, [_vp, _i32, _kvp, _vp, _i64, _i32, _vp, _i32, _i32,
+                                              _i32, _i32, _f32, _i32, _i32, _vp, _i32, _vp, _vp]),
     "paged_attn_run_causal": (ctypes.c_int, [_vp, _i32, _kvp, _vp, _i64, _i32, _vp, _i32, _i32, _i32,
                                              _i32, _f32, _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),
     "paged_attn_resolve_splits": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),

@@ -161,6 +161,28 @@ def paged_attn_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_tabl
     return out, lse
 
 
+def paged_attn_run_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           block_table: torch.Tensor, seq_lens: torch.Tensor, *, scale: float,
+                           out: torch.Tensor, lse: Optional[torch.Tensor] = None, window: int = 0,
+                           num_splits: int = 0, k_scale: float = 1.0, v_scale: float = 1.0):
+    """paged_attn_run with no workspace: the Split-KV partials go to the library's static
+    per-GPU scratch (the C entry point paged_attn_run_noalloc).  Nothing is allocated here
+    either, so `out` (and `lse`, if wanted) must be passed.  Calls that overlap in time on
+    one GPU share the scratch and race.  Returns (out, lse)."""
+    B, sq, Hq, D = q.shape
+    _check_paged_inputs(q, k, v, block_table, seq_lens)
+    desc = kv_desc(k, v, k_scale=k_scale, v_scale=v_scale)
+    _need(out, "out", (B, sq, Hq, D))
+    _need(lse, "lse", (B, sq, Hq), torch.float32)
+    _same_device(q.device, k=k, v=v, block_table=block_table, seq_lens=seq_lens, out=out, lse=lse)
+    W = block_table.shape[1]
+    check(load().paged_attn_run_noalloc(
+        q.data_ptr(), dtype_code(q.dtype), ctypes.byref(desc), block_table.data_ptr(),
+        block_table.stride(0), W, seq_lens.data_ptr(), B, sq, Hq, D, float(scale), int(window),
+        int(num_splits), out.data_ptr(), dtype_code(out.dtype), _ptr(lse), _stream(q.device)))
+    return out, lse
+
+
 def paged_attn_run_causal(q, k, v, block_table, seq_lens, **kw):
     """paged_attn_run with the bottom-right causal mask and an exact per-token window
     (the C entry point paged_attn_run_causal); same arguments and results."""
@@ -363,7 +385,8 @@ paged_attn_window_width = window_width
 __all__ = [
     "PagedAttnError", "dtype_code", "kv_desc", "kv_halves", "resolve_splits", "workspace_size", "plan",
     "new_workspace",
-    "paged_attn_run", "paged_attn_run_causal", "paged_attn_partial", "split_kv_combine",
+    "paged_attn_run", "paged_attn_run_causal", "paged_attn_run_noalloc", "paged_attn_partial",
+    "split_kv_combine",
     "segment_attn_combine", "paged_kv_write",
     "segment_attn_run", "segment_attn_workspace_size", "window_width", "paged_attn_describe",
     "paged_attn_describe_host", "paged_attn_plan", "paged_attn_resolve_splits",

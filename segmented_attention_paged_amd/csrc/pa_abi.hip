@@ -1,7 +1,7 @@
 // C ABI of the paged-attention library: argument checks, split planning,
-// workspace carving and kernel dispatch.  Host code only; it never allocates,
-// synchronizes or reads device memory, so every entry point can be captured
-// into a hipGraph.
+// workspace carving and kernel dispatch.  Host code (plus the device scratch
+// array of the allocation-free entry point); it never allocates, synchronizes
+// or reads device memory, so every entry point can be captured into a hipGraph.
 
 #include <algorithm>
 #include <cmath>
@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/paged_attn.h"
 #include "pa_kernels.h"
@@ -185,6 +186,52 @@ AttnParams paged_params(const void* q, const pa_kv_desc* kv, const int32_t* bloc
 
 }  // namespace
 
+// ---- allocation-free variant of paged_attn_run ------------------------------------
+// The Split-KV partials of paged_attn_run_noalloc live in this file-scope device
+// array instead of a caller workspace.  Each GPU the library runs on holds its
+// own copy (at its own address) until the process ends.  In host code the name
+// `scratch` is only a host-side stand-in: its device address is looked up once
+// per device with hipGetSymbolAddress and only that address is used.
+static __device__ __align__(256) char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device `stream` belongs to (the current
+// device for the null stream), looked up on the first call for that device
+// with that device current.
+int scratch_for_stream(hipStream_t stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PA_ENOTSUP, "device %d: the allocation-free scratch covers devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) return hip_fail(e2, "hipSetDevice");
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(PA_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char* pa_last_error(void) { return g_err; }
@@ -322,6 +369,31 @@ int paged_attn_run(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
   return run_paged(q, q_dtype, kv, block_table, bt_row_stride, bt_width, seq_lens, B, query_len, Hq,
                    D, scale, window, num_splits, out, out_dtype, lse, workspace, workspace_bytes,
                    stream, false);
+}
+
+int paged_attn_run_noalloc(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
+                           const int32_t* block_table, int64_t bt_row_stride, int32_t bt_width,
+                           const int32_t* seq_lens, int32_t B, int32_t query_len, int32_t Hq,
+                           int32_t D, float scale, int32_t window, int32_t num_splits, void* out,
+                           int32_t out_dtype, float* lse, hipStream_t stream) {
+  int rc = check_paged(q, q_dtype, kv, block_table, bt_row_stride, bt_width, seq_lens, B, query_len,
+                       Hq, D, scale);
+  if (rc != PA_OK) return rc;
+  if (B == 0 || query_len == 0) return ok();
+  const size_t need = paged_attn_workspace_size(B, query_len, Hq, kv->num_kv_heads, D,
+                                                kv->page_size, bt_width, window, num_splits);
+  void* ws = nullptr;
+  if (need > 0) {
+    if (need > PA_NOALLOC_SCRATCH_BYTES)
+      return fail(PA_EWORKSPACE,
+                  "paged_attn_run_noalloc: this shape needs %zu bytes of Split-KV partials, more "
+                  "than its %zu-byte scratch; use paged_attn_run with a workspace or fewer splits",
+                  need, (size_t)PA_NOALLOC_SCRATCH_BYTES);
+    rc = scratch_for_stream(stream, &ws);
+    if (rc != PA_OK) return rc;
+  }
+  return run_paged(q, q_dtype, kv, block_table, bt_row_stride, bt_width, seq_lens, B, query_len, Hq,
+                   D, scale, window, num_splits, out, out_dtype, lse, ws, need, stream, false);
 }
 
 int paged_attn_run_causal(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
