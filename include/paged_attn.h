@@ -167,12 +167,19 @@ int paged_attn_run_causal(const void* q, int32_t q_dtype, const pa_kv_desc* kv,
                           void* out, int32_t out_dtype, float* lse,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* The split count paged_attn_run resolves num_splits to for this shape (>= 1). */
+/* The split count paged_attn_run resolves num_splits to for this shape (>= 1).
+ * The fa_utils page exposes num_splits as the Split-KV knob and leaves the
+ * choice of splits to the kernel; the rule applied here for 0 (automatic) and
+ * -c (chunks of c pages) is this library's own, and depends on the visible
+ * page count, hence on Hkv, page_size, bt_width and window as well as on the
+ * query shape.  Host only; a malformed shape gives 1. */
 int32_t paged_attn_resolve_splits(int32_t B, int32_t query_len, int32_t Hq, int32_t Hkv,
                                   int32_t D, int32_t page_size, int32_t bt_width,
                                   int32_t window, int32_t num_splits);
 
-/* The launch plan paged_attn_run uses for this shape, written to plan[0..5]:
+/* The launch plan paged_attn_run uses for this shape (the Split-KV partition of
+ * the fa_utils page, num_splits, and the work decomposition around it),
+ * written to plan[0..5]:
  * split count S, pages per split (0 = ceil(visible pages / S)), 16-row MFMA
  * tiles per wave, waves per workgroup, row groups, workgroups in the grid.
  * Passing -plan[1] (or plan[0] when plan[1] == 0) as num_splits to
@@ -182,7 +189,10 @@ int paged_attn_plan(int32_t B, int32_t query_len, int32_t Hq, int32_t Hkv, int32
                     int32_t page_size, int32_t bt_width, int32_t window, int32_t num_splits,
                     int32_t* plan);
 
-/* Bytes of workspace paged_attn_run needs for this shape (0 when one pass). */
+/* Bytes of workspace paged_attn_run needs for this shape (0 when one pass): the
+ * fp32 partial outputs and LSEs of S splits, S as paged_attn_resolve_splits
+ * resolves num_splits.  It takes the cache geometry (Hkv, page_size, bt_width)
+ * and the window because the automatic split count depends on them. */
 size_t paged_attn_workspace_size(int32_t B, int32_t query_len, int32_t Hq, int32_t Hkv,
                                  int32_t D, int32_t page_size, int32_t bt_width,
                                  int32_t window, int32_t num_splits);
@@ -260,7 +270,12 @@ int32_t paged_attn_window_width(int32_t window, int32_t query_len, int32_t page_
                                 int32_t bt_width);
 
 /* The integer plan of paged_attn_run, computed on the device by the same code
- * the attention kernels run, so that it can be compared bit-exactly:
+ * the attention kernels run, so that it can be compared bit-exactly: the
+ * window restriction of the flashinfer_ts page (_restrict_to_window: the
+ * first visible page, the shortened length, the block table re-based to
+ * start there, its columns clamped to the table; _window_pages: the width of
+ * that table) and the Split-KV ranges of the fa_utils page (num_splits).
+ * Hkv, D and the query shape enter only through the automatic split count:
  *   out_lens  [B]            restricted length L_b - start_page * P
  *   out_table [B, out_width] restricted table: column j = table[b, min(start_page + j, bt_width-1)]
  *                            (out_width = paged_attn_window_width(...)); may be NULL
