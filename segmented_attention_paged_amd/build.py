@@ -83,6 +83,15 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     return LIB
 
 
+def device_asm(src: str, out: str) -> str:
+    """gfx950 assembly of one source file, compiled with the library's own flags."""
+    cmd = [_hipcc(), *COMMON, "--cuda-device-only", "-S", src, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--verbose", action="store_true")

@@ -271,14 +271,14 @@ __device__ __forceinline__ void attend_tile(const Frags<D, QT>& f,
       }
     }
   }
-  float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  float tmax = vmax(vmax(s[0], s[1]), vmax(s[2], s[3]));
   tmax = max_across_groups(tmax);
   // Lazy rescale: the reference max m_run only moves when some row of the
   // wave sees a logit more than kRescaleSlack above it, so p = 2^(s - m_run)
   // stays <= 2^kRescaleSlack and the O / l rescale is skipped on most tiles.
   // Softmax does not depend on the reference, only on it bounding the terms.
   if (__ballot(tmax > m_run + kRescaleSlack) != 0) {
-    const float m_new = fmaxf(m_run, tmax);
+    const float m_new = vmax(m_run, tmax);
     float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile (m_run = -inf)
     // a row that has seen no finite logit yet (m_new = -inf) keeps its zeros
     if constexpr (EMPTY_ROWS) alpha = m_new == kNegInf ? 1.f : alpha;
@@ -747,7 +747,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
       const int64_t orow = out_row(rr);
       float M = kNegInf;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w * rows_held + row]);
+      for (int w = 0; w < NW; ++w) M = vmax(M, red_m[w * rows_held + row]);
       float o[4] = {0.f, 0.f, 0.f, 0.f};
       float tot = 0.f;
       if (M != kNegInf) {
@@ -787,8 +787,16 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
 // fetches the chunk that belongs at its position.  Instruction j of a tile is
 // issued by wave j / (IPT / NW).
 // ================================================================================
+// Occupancy floor for the four- and eight-wave kernels: five waves per SIMD
+// (96 VGPRs) with 16-bit queries, six (80) with fp8 queries.  The causal bf16
+// kernel needs it to reach five without spilling; the two-wave kernels spill
+// under it and keep the default.
+template <int NW, int QT>
+constexpr int kSharedMinWaves = NW >= 4 ? (QT == K_FP8 ? 6 : 5) : 1;
+
 template <int D, int NW, int KV, int QT, int NBUF, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSharedMinWaves<NW, QT>)))
+void attn_shared_kernel(const AttnParams p) {
   using G = Geo<D, KV>;
   constexpr int KB = G::KB;
   constexpr int VPL = G::VPL;
@@ -1068,11 +1076,17 @@ __global__ __launch_bounds__(NW * 64) void attn_shared_kernel(const AttnParams p
     lse_base = p.lse + (int64_t)split * p.split_stride_lse;
     o_base = reinterpret_cast<float*>(p.out) + (int64_t)split * p.split_stride_o;
   }
-  const int rr = row0 + c16;
+  // The lane index is derived afresh here (v_mbcnt) instead of kept from the
+  // start, so no row-index value stays live across the tile loop: that frees
+  // the VGPR the dense bf16 kernel needs for five waves per SIMD.
+  int lane_now;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_now));
+  const int rr = row0 + (lane_now & 15);
   if (rr < p.R) {
     const int t = rr / p.G, gg = rr % p.G;
     const int64_t orow = ((int64_t)item * p.sq + t) * p.Hq + kvh * p.G + gg;
-    store_tile<D, true>(acc, m_run, l_run, p.v_scale, o_base, p.out_kind, lse_base, orow, p.partial, g4);
+    store_tile<D, true>(acc, m_run, l_run, p.v_scale, o_base, p.out_kind, lse_base, orow, p.partial,
+                        lane_now >> 4);
   }
 }
 

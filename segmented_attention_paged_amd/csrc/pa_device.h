@@ -107,6 +107,11 @@ __device__ __forceinline__ void fp8x4_to_16(uint32_t x, uint32_t& lo, uint32_t& 
 __device__ __forceinline__ uint32_t lo_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
 __device__ __forceinline__ uint32_t hi_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
 
+// max of two floats as gfx950's v_maximum_f32 (NaN-propagating): no quieting of
+// the operands first, which fmaxf needs in IEEE mode.  The attention logits it
+// sees are finite or -inf.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Reductions across the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48).
 // gfx950 lane swaps: permlane32_swap(a, b) exchanges lanes 32..63 of a with
 // lanes 0..31 of b; permlane16_swap(a, b) exchanges the odd 16-lane rows of a
@@ -115,12 +120,12 @@ __device__ __forceinline__ uint32_t hi_hi(uint32_t a, uint32_t b) { return (a >>
 __device__ __forceinline__ float xor32_pair(float x, bool max_op) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
-  return max_op ? fmaxf(a, b) : a + b;
+  return max_op ? vmax(a, b) : a + b;
 }
 __device__ __forceinline__ float xor16_pair(float x, bool max_op) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
-  return max_op ? fmaxf(a, b) : a + b;
+  return max_op ? vmax(a, b) : a + b;
 }
 __device__ __forceinline__ float max_across_groups(float x) { return xor32_pair(xor16_pair(x, true), true); }
 __device__ __forceinline__ float sum_across_groups(float x) { return xor32_pair(xor16_pair(x, false), false); }

@@ -386,3 +386,78 @@ def test_dead_segment_is_bitwise_inert(sap, fused):
     b2[2, 1] = 50.0
     out2, lse2 = sap.segment_attn_run(s.q, k2, v2, used, b2, bs=s.bs, local=s.local, fused=fused)
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16)) and torch.equal(lse1, lse2)
+
+
+# ---- logit scale sign --------------------------------------------------------------
+# A negative scale flips which keys dominate and a zero scale weighs every visible key
+# alike; both must follow the plain softmax of scale * q.k.
+@pytest.mark.parametrize("scale", [-0.09, 0.0, -1e-3])
+@pytest.mark.parametrize("name", ["decode_d128_g4", "block_sq16_window", "fp8_bf16q",
+                                  "fp8_sq16_window", "block_sq3_rt2"])
+def test_logit_scale_sign(sap, name, scale):
+    inp = _small(name)
+    inp.scale = scale
+    tol = TOL_FP8 if inp.kv_dtype == "fp8_e4m3" else TOL_BF16
+    for causal in (False, True):
+        for splits in (1, 3):
+            out, lse = run_paged(inp, num_splits=splits, causal=causal)
+            O, L = oracle_paged(inp, causal=causal)
+            compare(out, lse, O, L, tol, what=f"{name} scale={scale} causal={causal} S={splits}")
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_logit_scale_sign_fp8_query(sap, scale):
+    inp = make_paged(seed=29, poison=True, kv_dtype="fp8_e4m3", q_dtype="fp8_e4m3", B=3, sq=16,
+                     Hq=32, Hkv=8, D=128, P=16, seq_lens=[16, 257, 640]).to(DEV)
+    inp.scale = scale
+    out, lse = run_paged(inp, num_splits=0)
+    O, L = oracle_paged(inp)
+    compare(out, lse, O, L, TOL_FP8, what=f"fp8 q scale={scale}")
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+@pytest.mark.parametrize("fused", [True, False])
+def test_logit_scale_sign_segments(sap, scale, fused):
+    s = make_segments(seed=23, poison=True, zero_frac=0.25, name="sign", **SEG["seg_small"])
+    O, L = oracle.segment_attention(to_numpy_bits(s.q), to_numpy_bits(s.k), to_numpy_bits(s.v),
+                                    s.used.numpy(), s.bias.numpy(), topk=s.topk, bs=s.bs,
+                                    local=s.local, scale=scale)
+    d = s.to(DEV)
+    out, lse = sap.segment_attn_run(d.q, d.k, d.v, d.used, d.bias, bs=s.bs, local=s.local,
+                                    scale=scale, fused=fused)
+    compare(out, lse, O, L, TOL_BF16, what=f"segments scale={scale} fused={fused}")
+
+
+# ---- repeatability ----------------------------------------------------------------
+# Every kernel is a fixed order of operations: repeated calls on the same inputs must
+# agree bit for bit (a value read before the instruction producing it has finished
+# shows up here first).
+@pytest.mark.parametrize("name,splits", [("decode_d128_g4", 1), ("decode_d128_g4", 3),
+                                         ("decode_d64_g8", 0), ("block_sq16_window", 2),
+                                         ("block_sq3_rt2", 1), ("fp8_bf16q", 3),
+                                         ("fp8_sq16_window", 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_repeated_calls_are_bitwise_equal(sap, name, splits, causal):
+    inp = _small(name)
+    ref = None
+    for rep in range(12):
+        out, lse = run_paged(inp, num_splits=splits, causal=causal)
+        if ref is None:
+            ref = (out.clone(), lse.clone())
+            continue
+        assert torch.equal(out.view(torch.int16), ref[0].view(torch.int16)), f"rep {rep}"
+        assert torch.equal(lse.view(torch.int32), ref[1].view(torch.int32)), f"rep {rep}"
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_repeated_segment_calls_are_bitwise_equal(sap, fused):
+    s = make_segments(seed=11, poison=True, zero_frac=0.25, name="rep", **SEG["seg_g8"]).to(DEV)
+    ref = None
+    for rep in range(12):
+        out, lse = sap.segment_attn_run(s.q, s.k, s.v, s.used, s.bias, bs=s.bs, local=s.local,
+                                        fused=fused)
+        if ref is None:
+            ref = (out.clone(), lse.clone())
+            continue
+        assert torch.equal(out.view(torch.int16), ref[0].view(torch.int16)), f"rep {rep}"
+        assert torch.equal(lse.view(torch.int32), ref[1].view(torch.int32)), f"rep {rep}"
