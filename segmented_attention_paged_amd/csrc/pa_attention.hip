@@ -210,6 +210,69 @@ __device__ __forceinline__ void make_frags(const Raw<D, KV>& r, Frags<D, QT>& f)
   }
 }
 
+// K/V of one 16-slot tile straight into registers (attn_kernel's layout):
+// lane l loads the K pieces of key l%16 and the V values of keys 4*(l/16)+i.
+// kb / vb: slot 0 of the tile in K and V; tsb: bytes between slots.  Slots at
+// or past nvalid read slot 0 (inside the tile; masked out of S later).
+// Where a key's V share is 8 bytes per lane (fp8 with D = 128, 16-bit with
+// D = 64), V arrives as two 16-byte loads per lane instead of four 8-byte ones
+// (fewer load instructions per tile: fp8 Split-KV decode 358 -> 347 us): the
+// lane pair (2m, 2m+1) loads head dims 16m .. 16m+15 of keys 4*(l/16) + {0, 1}
+// (even lane) and {2, 3} (odd lane), and pair_v_regs swaps halves before use.
+template <int D, int KV>
+__device__ __forceinline__ void load_tile_regs(Raw<D, KV>& r, const char* kb, const char* vb,
+                                               uint32_t tsb, int nvalid, int g4, int c16) {
+  using G = Geo<D, KV>;
+  const uint32_t ks = c16 < nvalid ? c16 : 0;
+  const uint32_t koff = ks * tsb + 16 * g4;
+#pragma unroll
+  for (int i = 0; i < G::KLD; ++i) r.k[i] = stream_load16(kb + (koff + 64 * i));
+  if constexpr (G::VDW == 2) {
+    const int h = c16 & 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int key = 4 * g4 + 2 * h + i;
+      const uint32_t vs = key < nvalid ? key : 0;
+      const u32x4 x = stream_load16(vb + (vs * tsb + 16 * (c16 >> 1)));
+      r.v[2 * i][0] = x[0];
+      r.v[2 * i][1] = x[1];
+      r.v[2 * i + 1][0] = x[2];
+      r.v[2 * i + 1][1] = x[3];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t vs = 4 * g4 + i < nvalid ? 4 * g4 + i : 0;
+      load_v<G::VDW>(r.v[i], vb + (vs * tsb + G::VB * c16));
+    }
+  }
+}
+
+// Lane-pair exchange after 16-byte V loads (see load_tile_regs): afterwards
+// r.v[i] holds head dims 8*(l%16) .. +7 of key 4*(l/16) + i, as 8-byte loads
+// would deliver them.
+template <int D, int KV>
+__device__ __forceinline__ void pair_v_regs(Raw<D, KV>& r, int c16) {
+  const bool odd = (c16 & 1) != 0;
+  uint32_t keep[2][2], send[2][2], recv[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      keep[i][w] = odd ? r.v[2 * i + 1][w] : r.v[2 * i][w];
+      send[i][w] = odd ? r.v[2 * i][w] : r.v[2 * i + 1][w];
+      // quad_perm(1, 0, 3, 2): lanes 2m and 2m+1 swap
+      recv[i][w] = (uint32_t)__builtin_amdgcn_mov_dpp((int)send[i][w], 0xB1, 0xF, 0xF, false);
+    }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      r.v[i][w] = odd ? recv[i][w] : keep[i][w];
+      r.v[2 + i][w] = odd ? keep[i][w] : recv[i][w];
+    }
+}
+
 // Query fragments (B operand of S^T = K Q^T) for row tile starting at `row0`:
 // the same head dims per lane and register as the K operand of make_frags.
 template <int D, int KV, int QT>
@@ -573,64 +636,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   // Tile bases are wave-uniform (scalar registers); lanes add 32-bit offsets,
   // so each load is a scalar base plus one VGPR offset.
   const uint32_t tsb = (uint32_t)ts_b;  // 16 * tsb < 2^31 (checked at the boundary)
-  // 8 bytes of V per key and lane (fp8 with D = 128, 16-bit with D = 64): V
-  // arrives as two 16-byte loads per lane instead of four 8-byte ones (fewer
-  // load instructions per tile: fp8 Split-KV decode 358 -> 347 us)
   constexpr bool kPairV = G::VDW == 2;
   auto load_tile = [&](Raw<D, KV>& r, const TileInfo& ti) {
     // offsets from the kernel-argument pointers keep the global address space
-    const char* kb = p.k + uniform64(ti.kp - p.k);
-    const char* vb = p.k + uniform64(ti.vp - p.k);
-    const uint32_t ks = c16 < ti.nvalid ? c16 : 0;  // invalid slots read slot 0 (masked later)
-    const uint32_t koff = ks * tsb + 16 * g4;
-#pragma unroll
-    for (int i = 0; i < G::KLD; ++i) r.k[i] = stream_load16(kb + (koff + 64 * i));
-    if constexpr (kPairV) {
-      // 16-byte V loads: the lane pair (2m, 2m+1) loads head dims 16m .. 16m+15
-      // of keys 4*(l/16) + {0, 1} (even lane) and {2, 3} (odd lane); pair_v
-      // swaps halves before use so each lane holds its 8 dims of all 4 keys
-      const int h = c16 & 1;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int key = 4 * g4 + 2 * h + i;
-        const uint32_t vs = key < ti.nvalid ? key : 0;
-        const u32x4 x = stream_load16(vb + (vs * tsb + 16 * (c16 >> 1)));
-        r.v[2 * i][0] = x[0];
-        r.v[2 * i][1] = x[1];
-        r.v[2 * i + 1][0] = x[2];
-        r.v[2 * i + 1][1] = x[3];
-      }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t vs = 4 * g4 + i < ti.nvalid ? 4 * g4 + i : 0;
-      load_v<G::VDW>(r.v[i], vb + (vs * tsb + G::VB * c16));
-    }
+    load_tile_regs<D, KV>(r, p.k + uniform64(ti.kp - p.k), p.k + uniform64(ti.vp - p.k), tsb,
+                          ti.nvalid, g4, c16);
   };
-  // Lane-pair exchange after 16-byte V loads (see load_tile): afterwards
-  // r.v[i] holds head dims 8*(l%16) .. +7 of key 4*(l/16) + i, as the 8-byte
-  // loads deliver them.
-  auto pair_v = [&](Raw<D, KV>& r) {
-    const bool odd = (c16 & 1) != 0;
-    uint32_t keep[2][2], send[2][2], recv[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        keep[i][w] = odd ? r.v[2 * i + 1][w] : r.v[2 * i][w];
-        send[i][w] = odd ? r.v[2 * i][w] : r.v[2 * i + 1][w];
-        // quad_perm(1, 0, 3, 2): lanes 2m and 2m+1 swap
-        recv[i][w] = (uint32_t)__builtin_amdgcn_mov_dpp((int)send[i][w], 0xB1, 0xF, 0xF, false);
-      }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        r.v[i][w] = odd ? recv[i][w] : keep[i][w];
-        r.v[2 + i][w] = odd ? keep[i][w] : recv[i][w];
-      }
-  };
+  auto pair_v = [&](Raw<D, KV>& r) { pair_v_regs<D, KV>(r, c16); };
 
   f32x4 acc[RT][VPL];
   float m_run[RT], l_run[RT];
