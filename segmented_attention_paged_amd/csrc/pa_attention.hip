@@ -86,8 +86,10 @@ struct TileInfo {
   const char* kp;  // byte address of slot 0 of the tile, head kvh, in K
   const char* vp;  // same in V
   int nvalid;      // slots [0, nvalid) hold visible keys (1..16)
-  float bias;      // log2-domain logit bias of the tile (fused segments)
-  int key0;        // key index of slot 0 (restricted numbering; paged modes)
+  float bias;      // log2-domain logit bias of the tile (segment partials: 0)
+  int key0;        // key index of slot 0 (restricted numbering; paged modes);
+                   // fused segments: position of slot 0 among the query's live keys
+  int g0;          // fused segments: segment holding slot 0
 };
 
 // Causal query block (paged): row r of a tile sees keys [lo, hi] of the
@@ -301,14 +303,18 @@ __device__ __forceinline__ void load_q(typename QTypes<QT>::QOp (&qf)[D / 32], c
 // EMPTY_ROWS: a row may have seen only -inf logits so far (causal rows before
 // their first key; fused segments whose bias is -inf), so its running max can
 // still be -inf and the exponent reference must stay finite.
-template <int D, int QT, bool CAUSAL = false, bool EMPTY_ROWS = CAUSAL, typename Hook = NoHook,
-          typename VHook = NoHook>
+// KEY_BIAS: each of the lane's four keys carries its own bias (kbias[i] for key
+// 4*g4 + i: a tile packed from several segments); otherwise every key of the
+// tile carries `bias`.
+template <int D, int QT, bool CAUSAL = false, bool EMPTY_ROWS = CAUSAL, bool KEY_BIAS = false,
+          typename Hook = NoHook, typename VHook = NoHook>
 __device__ __forceinline__ void attend_tile(const Frags<D, QT>& f,
                                             const typename QTypes<QT>::QOp (&qf)[D / 32],
                                             f32x4 (&acc)[D / 16], float& m_run, float& l_run,
                                             float scale_log2, float bias, int nvalid, int g4,
                                             int key0 = 0, RowMask rm = RowMask{false, 0, 0},
-                                            const Hook& mid = Hook{}, const VHook& vload = VHook{}) {
+                                            const Hook& mid = Hook{}, const VHook& vload = VHook{},
+                                            f32x4 kbias = f32x4{0.f, 0.f, 0.f, 0.f}) {
   f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kc = 0; kc < D / 32; ++kc) sacc = qk_mfma<QT>(f.kf[kc], qf[kc], sacc);
@@ -319,7 +325,7 @@ __device__ __forceinline__ void attend_tile(const Frags<D, QT>& f,
   }
   float s[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s[i] = sacc[i] * scale_log2 + bias;
+  for (int i = 0; i < 4; ++i) s[i] = sacc[i] * scale_log2 + (KEY_BIAS ? kbias[i] : bias);
   if (nvalid < 16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -530,10 +536,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   PagedRange pr{};
   int64_t seg_tok0 = 0;
   int seg_used = 0;
-  // fused segments: lane g describes segment g
-  int f_used = 0, f_tiles = 0, f_cum_end = 0x7fffffff;
-  int64_t f_base = 0;
+  // fused segments: lane g describes segment g; the live keys of the query's
+  // segments are numbered in segment order and cut into 16-key tiles, so a
+  // tile may span segments (only the query's last tile is partly filled)
+  int f_cum_end = 0x7fffffff, f_cum_start = 0x7fffffff, f_adj = 0;
   float f_bias = 0.f;
+  int n_keys = 0;
+  int64_t f_qoff_b = 0;  // byte offset of the query's first row, at this kv head
 
   if constexpr (MODE == MODE_PAGED) {
     pr = paged_range(p, item, split);
@@ -551,23 +560,28 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   } else {
     const int Gs = p.topk + 1;
     const int n = item;
+    int u = 0;
     if (lane < Gs) {
       const int cap = lane < p.topk ? p.bs : p.local;
-      int u = p.used[(int64_t)n * Gs + lane];
+      u = p.used[(int64_t)n * Gs + lane];
       u = u < 0 ? 0 : (u > cap ? cap : u);
-      f_used = u;
-      f_tiles = (u + 15) >> 4;
-      f_base = (int64_t)n * (p.topk * p.bs + p.local) + (lane < p.topk ? lane * p.bs : p.topk * p.bs);
       f_bias = lane < p.topk ? p.bias[(int64_t)n * p.topk + lane] * kLog2e : 0.f;
     }
-    int cum = f_tiles;  // inclusive prefix sum of tile counts across lanes
+    int cum = u;  // inclusive prefix sum of live keys across lanes
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int o = __shfl_up(cum, off, 64);
       if (lane >= off) cum += o;
     }
-    n_tiles = __shfl(cum, 63, 64);
-    f_cum_end = lane < Gs ? cum : 0x7fffffff;
+    n_keys = __shfl(cum, 63, 64);
+    n_tiles = (n_keys + 15) >> 4;
+    if (lane < Gs) {
+      f_cum_end = cum;
+      f_cum_start = cum - u;
+      // row of the query holding live key j of segment `lane`: j + f_adj
+      f_adj = (lane < p.topk ? lane * p.bs : p.topk * p.bs) - f_cum_start;
+    }
+    f_qoff_b = (int64_t)n * (p.topk * p.bs + p.local) * ts_b + head_off_b;
     qb = n;
   }
 
@@ -588,6 +602,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
     TileInfo ti;
     ti.bias = 0.f;
     ti.key0 = 0;
+    ti.g0 = 0;
     if constexpr (MODE == MODE_PAGED) {
       if (k - k0 >= 64) {
         k0 = k;
@@ -613,22 +628,14 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
       ti.kp = p.k + off;
       ti.vp = p.v + off;
     } else {
-      // segment holding tile `it`: the number of segments that end at or before
-      // it.  The index is wave-uniform, so its fields are read with v_readlane
-      // (scalar reads, no LDS round trip on the way to the tile's loads).
-      const int gsel = __builtin_amdgcn_readfirstlane(__builtin_popcountll(__ballot(f_cum_end <= it)));
-      const int cend = __builtin_amdgcn_readlane(f_cum_end, gsel);
-      const int ntl = __builtin_amdgcn_readlane(f_tiles, gsel);
-      const int ul = __builtin_amdgcn_readlane(f_used, gsel);
-      const int64_t base = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(f_base >> 32), gsel) << 32) |
-                                     (uint32_t)__builtin_amdgcn_readlane((int)f_base, gsel));
-      ti.bias = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f_bias), gsel));
-      const int lt = it - (cend - ntl);
-      const int nv = ul - 16 * lt;
+      // live keys 16*it .. 16*it+15; slot 0 lies in the first segment that
+      // ends after it (segments are found per key when the tile is loaded)
+      ti.key0 = 16 * it;
+      ti.g0 = __builtin_amdgcn_readfirstlane(__builtin_popcountll(__ballot(f_cum_end <= ti.key0)));
+      const int nv = n_keys - ti.key0;
       ti.nvalid = nv > 16 ? 16 : nv;
-      const int64_t off = (base + 16 * lt) * ts_b + head_off_b;
-      ti.kp = p.k + off;
-      ti.vp = p.v + off;
+      ti.kp = p.k + f_qoff_b;
+      ti.vp = p.v + f_qoff_b;
     }
     return ti;
   };
@@ -637,10 +644,59 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   // so each load is a scalar base plus one VGPR offset.
   const uint32_t tsb = (uint32_t)ts_b;  // 16 * tsb < 2^31 (checked at the boundary)
   constexpr bool kPairV = G::VDW == 2;
+  // Fused segments: per-lane field of the segment holding each of the lane's
+  // keys 16*it + d[j] (d[j] < 16).  Only segments that start inside the tile
+  // are visited (a wave-uniform loop, usually 0-2 rounds): lane g holds
+  // segment g's fields, read with v_readlane.
+  auto seg_field = [&](const TileInfo& ti, const int (&d)[5], int field, int (&out)[5]) {
+    const int v0 = __builtin_amdgcn_readlane(field, ti.g0);
+#pragma unroll
+    for (int j = 0; j < 5; ++j) out[j] = v0;
+    for (int g = ti.g0 + 1; g <= p.topk; ++g) {
+      const int thr = __builtin_amdgcn_readlane(f_cum_start, g) - ti.key0;
+      if (thr >= 16) break;
+      const int vg = __builtin_amdgcn_readlane(field, g);
+#pragma unroll
+      for (int j = 0; j < 5; ++j) out[j] = d[j] >= thr ? vg : out[j];
+    }
+  };
   auto load_tile = [&](Raw<D, KV>& r, const TileInfo& ti) {
-    // offsets from the kernel-argument pointers keep the global address space
-    load_tile_regs<D, KV>(r, p.k + uniform64(ti.kp - p.k), p.k + uniform64(ti.vp - p.k), tsb,
-                          ti.nvalid, g4, c16);
+    if constexpr (MODE != MODE_SEGMENT_FUSED) {
+      // offsets from the kernel-argument pointers keep the global address space
+      load_tile_regs<D, KV>(r, p.k + uniform64(ti.kp - p.k), p.k + uniform64(ti.vp - p.k), tsb,
+                            ti.nvalid, g4, c16);
+    } else {
+      // key slots: K of key c16, V of keys 4*g4 + i (slots past the live keys read key 0)
+      int d[5], row[5];
+      d[0] = c16 < ti.nvalid ? c16 : 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[1 + i] = 4 * g4 + i < ti.nvalid ? 4 * g4 + i : 0;
+      seg_field(ti, d, f_adj, row);
+#pragma unroll
+      for (int j = 0; j < 5; ++j) row[j] += ti.key0 + d[j];
+      const char* kq = p.k + uniform64(ti.kp - p.k);
+      const char* vq = p.k + uniform64(ti.vp - p.k);
+      const uint64_t koff = (uint64_t)(uint32_t)row[0] * tsb + 16 * g4;
+#pragma unroll
+      for (int i = 0; i < G::KLD; ++i) r.k[i] = stream_load16(kq + (koff + 64 * i));
+      if constexpr (G::VDW == 2) {
+        // as load_tile_regs: the lane pair (2m, 2m+1) loads keys 4*g4 + {0, 1} / {2, 3}
+        const bool h = (c16 & 1) != 0;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int rw = h ? row[3 + i] : row[1 + i];
+          const u32x4 x = stream_load16(vq + ((uint64_t)(uint32_t)rw * tsb + 16 * (c16 >> 1)));
+          r.v[2 * i][0] = x[0];
+          r.v[2 * i][1] = x[1];
+          r.v[2 * i + 1][0] = x[2];
+          r.v[2 * i + 1][1] = x[3];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          load_v<G::VDW>(r.v[i], vq + ((uint64_t)(uint32_t)row[1 + i] * tsb + G::VB * c16));
+      }
+    }
   };
   auto pair_v = [&](Raw<D, KV>& r) { pair_v_regs<D, KV>(r, c16); };
 
@@ -670,11 +726,22 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   }
   auto attend = [&](const Frags<D, QT>& f, const TileInfo& ti) {
     const bool on = CAUSAL && (ti.key0 + 15 > hi_min || ti.key0 < lo_max);
+    f32x4 kbias = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (MODE == MODE_SEGMENT_FUSED) {
+      // bias of the segment of each of the lane's keys 4*g4 + i (the S^T layout)
+      int d[5], b[5];
+      d[0] = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[1 + i] = 4 * g4 + i;
+      seg_field(ti, d, __float_as_int(f_bias), b);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kbias[i] = __int_as_float(b[1 + i]);
+    }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
-      attend_tile<D, QT, CAUSAL, CAUSAL || MODE == MODE_SEGMENT_FUSED>(
+      attend_tile<D, QT, CAUSAL, CAUSAL || MODE == MODE_SEGMENT_FUSED, MODE == MODE_SEGMENT_FUSED>(
           f, qf[rt], acc[rt], m_run[rt], l_run[rt], p.qk_scale_log2, ti.bias, ti.nvalid, g4,
-          ti.key0, RowMask{on, row_hi[rt], row_lo[rt]});
+          ti.key0, RowMask{on, row_hi[rt], row_lo[rt]}, NoHook{}, NoHook{}, kbias);
   };
 
   // main loop: tile k+1 is in flight while tile k is computed
