@@ -74,24 +74,34 @@ def read_counters(workload: str):
         return None
 
 
-def time_events(fn, steps: int, warmup: int, flush=None):
-    """Average ms per call on the current stream (HIP events); optional cache flush between calls."""
+def time_events(fn, steps: int, warmup: int, flush=None, rounds: int = 1):
+    """ms per call on the current stream (HIP events); optional cache flush between calls.
+
+    Back to back: the average over `steps` calls, and with rounds > 1 the median of
+    `rounds` such averages.  With a flush each call is timed alone between its own
+    events and the median call is returned (rounds is then ignored).  Medians keep a
+    stall of the launching host thread out of a kernel's figure."""
+    import statistics
+
     import torch
 
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     if flush is None:
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        s.record()
-        for _ in range(steps):
-            fn()
-        e.record()
-        torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) * 1e3 / steps
-        return s.elapsed_time(e) / steps, wall
-    total = 0.0
+        avgs, walls = [], []
+        for _ in range(rounds):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            s.record()
+            for _ in range(steps):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            walls.append((time.perf_counter() - t0) * 1e3 / steps)
+            avgs.append(s.elapsed_time(e) / steps)
+        return statistics.median(avgs), statistics.median(walls)
+    per_call = []
     t0 = time.perf_counter()
     for _ in range(steps):
         flush()
@@ -100,8 +110,8 @@ def time_events(fn, steps: int, warmup: int, flush=None):
         fn()
         e.record()
         torch.cuda.synchronize()
-        total += s.elapsed_time(e)
-    return total / steps, (time.perf_counter() - t0) * 1e3 / steps
+        per_call.append(s.elapsed_time(e))
+    return statistics.median(per_call), (time.perf_counter() - t0) * 1e3 / steps
 
 
 _FLUSH = {}
@@ -294,7 +304,7 @@ def measure_paged(name: str, causal: bool, steps: int, warmup: int, cpu_seconds:
     pb = pb or PagedBench(name, causal=causal)
     inp = pb.inp
     flush = mall_flush(pb.kv_bytes)
-    step_ms, _ = time_events(pb.step, steps, warmup, flush)
+    step_ms, _ = time_events(pb.step, steps, warmup, flush, rounds=3)
     res = {
         "workload": name, "causal": causal, "B": inp.B, "query_len": inp.sq, "Hq": inp.Hq,
         "Hkv": inp.Hkv, "head_dim": inp.D, "kv_dtype": inp.kv_dtype,
@@ -305,7 +315,7 @@ def measure_paged(name: str, causal: bool, steps: int, warmup: int, cpu_seconds:
         "kv_gbps": pb.kv_bytes / step_ms / 1e6, "hbm_frac": pb.kv_bytes / step_ms / 1e6 / HBM_PEAK_GBPS,
     }
     if not causal:
-        kern_ms, _ = time_events(pb.kernel, steps, warmup, flush)
+        kern_ms, _ = time_events(pb.kernel, steps, warmup, flush, rounds=3)
         res.update(kernel_us=kern_ms * 1e3, kernel_gbps=pb.kv_bytes / kern_ms / 1e6,
                    kernel_hbm_frac=pb.kv_bytes / kern_ms / 1e6 / HBM_PEAK_GBPS)
     if inp.sq >= 16:
