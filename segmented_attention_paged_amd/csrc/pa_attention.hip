@@ -934,7 +934,11 @@ void attn_shared_kernel(const AttnParams p) {
   const int32_t* trow = p.block_table + (int64_t)item * p.bt_stride;
   auto table_batch = [&](int first) -> int32_t {
     const int kl = first + lane;
-    return trow[table_column(pr.sv, pr.sr.first_page + (pr.TPP == 1 ? kl : kl / pr.TPP), p.bt_width)];
+    // the divisor is passed through an opaque copy so its reciprocal is worked
+    // out here, once per 64 tiles, instead of being held across the tile loop
+    int tpp = pr.TPP;
+    asm volatile("" : "+s"(tpp));
+    return trow[table_column(pr.sv, pr.sr.first_page + (tpp == 1 ? kl : kl / tpp), p.bt_width)];
   };
   int32_t phys_vec = table_batch(0);
   int k0 = 0;
@@ -1162,7 +1166,9 @@ void attn_shared_kernel(const AttnParams p) {
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_now));
   const int rr = row0 + (lane_now & 15);
   if (rr < p.R) {
-    const int t = rr / p.G, gg = rr % p.G;
+    int G = p.G;  // opaque copy: no reciprocal of G kept from before the loop
+    asm volatile("" : "+s"(G));
+    const int t = rr / G, gg = rr % G;
     const int64_t orow = ((int64_t)item * p.sq + t) * p.Hq + kvh * p.G + gg;
     store_tile<D, true>(acc, m_run, l_run, p.v_scale, o_base, p.out_kind, lse_base, orow, p.partial,
                         lane_now >> 4);
