@@ -2,7 +2,9 @@
 //
 // Rows of a work item are the G query heads of one kv head times the query
 // block (row r -> token r / G, head kvh*G + r % G), packed into 16-row MFMA
-// tiles.  Keys are consumed in tiles of 16 slots of one page.
+// tiles.  Keys are consumed in tiles of 16 slots of one page (paged modes), of
+// one segment (segment partials), or of a query's live keys numbered across its
+// segments (fused segments: a tile may span segments).
 //
 // Per 16-key tile and 16-row tile:
 //   S^T = K Q^T      D/32 x v_mfma_f32_16x16x32_{bf16,f16}, or _fp8_fp8 on the
