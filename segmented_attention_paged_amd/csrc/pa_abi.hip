@@ -499,6 +499,11 @@ int segment_attn_run(const void* q, int32_t q_dtype, const void* k, const void* 
     p.out_kind = out_dtype;
     p.lse = lse;
     p.partial = 0;
+    if (dash_shared_supported(D, kv_dtype, G, Hkv)) {
+      hipError_t e = launch_dash_shared(p, D, kv_dtype, stream);
+      if (e != hipSuccess) return hip_fail(e, "segment attention launch");
+      return ok();
+    }
     const LaunchShape ls{D, kv_dtype, q_dtype, RT, NW, MODE_SEGMENT_FUSED, 0, 0};
     hipError_t e = launch_attention(p, ls, (int64_t)N * Hkv * RG, stream);
     if (e != hipSuccess) return hip_fail(e, "segment attention launch");

@@ -497,6 +497,67 @@ __device__ __forceinline__ int32_t load_phys(const AttnParams& p, const int32_t*
   return ph < 0 ? 0 : (ph >= p.num_pages ? p.num_pages - 1 : ph);
 }
 
+// Fused segments of query n (dash_attention page, flash_dash_attention): lane
+// g <= topk describes segment g (the topk remote segments, then the local
+// one).  The query's live keys are numbered in segment order, so live key j
+// of segment g is key cum_start + j and sits at row j + adj of the query.
+struct SegLanes {
+  int cum_end = 0x7fffffff;    // live keys of segments 0..g
+  int cum_start = 0x7fffffff;  // live keys before segment g
+  int adj = 0;                 // segment g's first row minus cum_start
+  float bias = 0.f;            // segment bias in log2 units (local segment: 0)
+  int n_keys = 0;              // live keys of the query (every lane)
+};
+
+__device__ __forceinline__ SegLanes seg_lanes(const AttnParams& p, int n, int lane) {
+  SegLanes s;
+  const int Gs = p.topk + 1;
+  int u = 0;
+  if (lane < Gs) {
+    const int cap = lane < p.topk ? p.bs : p.local;
+    u = p.used[(int64_t)n * Gs + lane];
+    u = u < 0 ? 0 : (u > cap ? cap : u);
+    s.bias = lane < p.topk ? p.bias[(int64_t)n * p.topk + lane] * kLog2e : 0.f;
+  }
+  int cum = u;  // inclusive prefix sum of live keys across lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(cum, off, 64);
+    if (lane >= off) cum += o;
+  }
+  s.n_keys = __shfl(cum, 63, 64);
+  if (lane < Gs) {
+    s.cum_end = cum;
+    s.cum_start = cum - u;
+    s.adj = (lane < p.topk ? lane * p.bs : p.topk * p.bs) - s.cum_start;
+  }
+  return s;
+}
+
+// Segment holding live key `key` (wave-uniform key).
+__device__ __forceinline__ int seg_of_key(const SegLanes& s, int key) {
+  return __builtin_amdgcn_readfirstlane(__builtin_popcountll(__ballot(s.cum_end <= key)));
+}
+
+// Per-lane `field` (held by lane g for segment g) of the segment holding each
+// of the lane's keys key0 + d[j], d[j] < 16, where g0 holds key0.  Only the
+// segments that start inside the tile are visited: a wave-uniform loop,
+// usually 0-2 rounds.
+template <int N>
+__device__ __forceinline__ void seg_field(const SegLanes& s, int topk, int key0, int g0,
+                                          const int (&d)[N], int field, int (&out)[N]) {
+  const int v0 = __builtin_amdgcn_readlane(field, g0);
+#pragma unroll
+  for (int j = 0; j < N; ++j) out[j] = v0;
+  for (int g = g0 + 1; g <= topk; ++g) {
+    const int thr = __builtin_amdgcn_readlane(s.cum_start, g) - key0;
+    if (thr >= 16) break;
+    const int vg = __builtin_amdgcn_readlane(field, g);
+#pragma unroll
+    for (int j = 0; j < N; ++j) out[j] = d[j] >= thr ? vg : out[j];
+  }
+}
+
 }  // namespace
 
 // ================================================================================
@@ -538,12 +599,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   PagedRange pr{};
   int64_t seg_tok0 = 0;
   int seg_used = 0;
-  // fused segments: lane g describes segment g; the live keys of the query's
-  // segments are numbered in segment order and cut into 16-key tiles, so a
-  // tile may span segments (only the query's last tile is partly filled)
-  int f_cum_end = 0x7fffffff, f_cum_start = 0x7fffffff, f_adj = 0;
-  float f_bias = 0.f;
-  int n_keys = 0;
+  // fused segments: the live keys of the query's segments are numbered in
+  // segment order and cut into 16-key tiles, so a tile may span segments (only
+  // the query's last tile is partly filled)
+  SegLanes sl;
   int64_t f_qoff_b = 0;  // byte offset of the query's first row, at this kv head
 
   if constexpr (MODE == MODE_PAGED) {
@@ -560,29 +619,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
     n_tiles = (u + 15) >> 4;
     qb = n;
   } else {
-    const int Gs = p.topk + 1;
     const int n = item;
-    int u = 0;
-    if (lane < Gs) {
-      const int cap = lane < p.topk ? p.bs : p.local;
-      u = p.used[(int64_t)n * Gs + lane];
-      u = u < 0 ? 0 : (u > cap ? cap : u);
-      f_bias = lane < p.topk ? p.bias[(int64_t)n * p.topk + lane] * kLog2e : 0.f;
-    }
-    int cum = u;  // inclusive prefix sum of live keys across lanes
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(cum, off, 64);
-      if (lane >= off) cum += o;
-    }
-    n_keys = __shfl(cum, 63, 64);
-    n_tiles = (n_keys + 15) >> 4;
-    if (lane < Gs) {
-      f_cum_end = cum;
-      f_cum_start = cum - u;
-      // row of the query holding live key j of segment `lane`: j + f_adj
-      f_adj = (lane < p.topk ? lane * p.bs : p.topk * p.bs) - f_cum_start;
-    }
+    sl = seg_lanes(p, n, lane);
+    n_tiles = (sl.n_keys + 15) >> 4;
     f_qoff_b = (int64_t)n * (p.topk * p.bs + p.local) * ts_b + head_off_b;
     qb = n;
   }
@@ -633,8 +672,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
       // live keys 16*it .. 16*it+15; slot 0 lies in the first segment that
       // ends after it (segments are found per key when the tile is loaded)
       ti.key0 = 16 * it;
-      ti.g0 = __builtin_amdgcn_readfirstlane(__builtin_popcountll(__ballot(f_cum_end <= ti.key0)));
-      const int nv = n_keys - ti.key0;
+      ti.g0 = seg_of_key(sl, ti.key0);
+      const int nv = sl.n_keys - ti.key0;
       ti.nvalid = nv > 16 ? 16 : nv;
       ti.kp = p.k + f_qoff_b;
       ti.vp = p.v + f_qoff_b;
@@ -646,22 +685,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
   // so each load is a scalar base plus one VGPR offset.
   const uint32_t tsb = (uint32_t)ts_b;  // 16 * tsb < 2^31 (checked at the boundary)
   constexpr bool kPairV = G::VDW == 2;
-  // Fused segments: per-lane field of the segment holding each of the lane's
-  // keys 16*it + d[j] (d[j] < 16).  Only segments that start inside the tile
-  // are visited (a wave-uniform loop, usually 0-2 rounds): lane g holds
-  // segment g's fields, read with v_readlane.
-  auto seg_field = [&](const TileInfo& ti, const int (&d)[5], int field, int (&out)[5]) {
-    const int v0 = __builtin_amdgcn_readlane(field, ti.g0);
-#pragma unroll
-    for (int j = 0; j < 5; ++j) out[j] = v0;
-    for (int g = ti.g0 + 1; g <= p.topk; ++g) {
-      const int thr = __builtin_amdgcn_readlane(f_cum_start, g) - ti.key0;
-      if (thr >= 16) break;
-      const int vg = __builtin_amdgcn_readlane(field, g);
-#pragma unroll
-      for (int j = 0; j < 5; ++j) out[j] = d[j] >= thr ? vg : out[j];
-    }
-  };
   auto load_tile = [&](Raw<D, KV>& r, const TileInfo& ti) {
     if constexpr (MODE != MODE_SEGMENT_FUSED) {
       // offsets from the kernel-argument pointers keep the global address space
@@ -673,7 +696,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
       d[0] = c16 < ti.nvalid ? c16 : 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) d[1 + i] = 4 * g4 + i < ti.nvalid ? 4 * g4 + i : 0;
-      seg_field(ti, d, f_adj, row);
+      seg_field(sl, p.topk, ti.key0, ti.g0, d, sl.adj, row);
 #pragma unroll
       for (int j = 0; j < 5; ++j) row[j] += ti.key0 + d[j];
       const char* kq = p.k + uniform64(ti.kp - p.k);
@@ -735,7 +758,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
       d[0] = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) d[1 + i] = 4 * g4 + i;
-      seg_field(ti, d, __float_as_int(f_bias), b);
+      seg_field(sl, p.topk, ti.key0, ti.g0, d, __float_as_int(sl.bias), b);
 #pragma unroll
       for (int i = 0; i < 4; ++i) kbias[i] = __int_as_float(b[1 + i]);
     }
@@ -1177,6 +1200,175 @@ void attn_shared_kernel(const AttnParams p) {
   }
 }
 
+// ================================================================================
+// dash_shared_kernel: fused DASH attention (dash_attention page,
+// flash_dash_attention: one query against the valid rows of its gathered
+// segments, each segment's logits shifted by its bias) with the K and V rows of
+// HP kv heads staged through a two-stage LDS ring.
+//   work item:  (query, group of HP consecutive kv heads); the group's part of
+//               a token row (HP*D contiguous elements of K, the same of V) is
+//               fetched by direct-to-LDS loads of 16-byte chunks.
+//   waves:      HP, wave w serving kv head w of the group (its G query heads
+//               are the rows of one 16-row tile).
+//   keys:       the query's live keys numbered across its segments, 16 per
+//               tile (as the fused mode of attn_kernel); slots past the last
+//               live key fetch the tile's first key and are masked.
+// Each staged head uses attn_shared_kernel's tile layout (Geo::chunk_pos).
+// Tile k sits in stage k % 2.  A wave reads all of its K and V operands as
+// soon as the tile has landed; once every wave has, the stage takes tile k+2,
+// so two tiles are in flight while a wave computes or waits.
+// ================================================================================
+template <int D, int KV, int HP>
+__global__ __launch_bounds__(HP * 64) void dash_shared_kernel(const AttnParams p) {
+  constexpr int NW = HP;
+  using G = Geo<D, KV>;
+  constexpr int KB = G::KB;
+  constexpr int VPL = G::VPL;
+  constexpr int SUB = G::TILE_BYTES;     // one kv head's staged tile
+  constexpr int IPW = G::IPT;            // direct-to-LDS loads per wave per tile
+  static_assert(KV != K_FP8, "16-bit K/V only");
+  static_assert(SUB % 1024 == 0, "each 1 KiB load stays inside one head's staged tile");
+  constexpr int QT = KV;
+  __shared__ __attribute__((aligned(1024))) char ring0[HP * SUB];
+  __shared__ __attribute__((aligned(1024))) char ring1[HP * SUB];
+  auto stage_buf = [&](auto sc) -> char* {
+    if constexpr (decltype(sc)::value == 0) return ring0;
+    else return ring1;
+  };
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int g4 = lane >> 4;
+  const int c16 = lane & 15;
+
+  const int groups = p.Hkv / HP;
+  const int n = (int)(blockIdx.x / (uint32_t)groups);
+  const int grp = (int)(blockIdx.x % (uint32_t)groups);
+  const int kvh = grp * HP + wave;
+
+  const SegLanes sl = seg_lanes(p, n, lane);
+  const int n_tiles = (sl.n_keys + 15) >> 4;
+  const int64_t ts_b = p.token_stride * KB;
+  // the group's part of the query's first row, in K (V adds the V - K distance)
+  const int64_t qoff_b = (int64_t)n * (p.topk * p.bs + p.local) * ts_b +
+                         (int64_t)grp * HP * p.head_stride * KB;
+
+  typename QTypes<QT>::QOp qf[D / 32];
+  load_q<D, KV, QT>(qf, p.q, 0, p.R, p.G, kvh, n, 1, p.Hq, g4, c16);
+
+  // Lane constants of this wave's loads: load u writes LDS chunk position
+  // 64*(wave*IPW + u) + lane of the stage, which holds chunk c of key slot t
+  // of the wave's own head (heads one after another, each in
+  // attn_shared_kernel's layout).
+  const int64_t vk = p.v - p.k;
+  int64_t src_c[IPW];
+  int src_t[IPW];
+#pragma unroll
+  for (int u = 0; u < IPW; ++u) {
+    const int q = 64 * u + lane;
+    const int t = q / G::CPK;
+    const int c = (q % G::CPK) ^ G::swz(t, q % G::CPK);
+    src_c[u] = (c < G::CPK / 2 ? 16 * c : vk + 16 * (c - G::CPK / 2)) +
+               (int64_t)wave * p.head_stride * KB;
+    src_t[u] = t;
+  }
+  const uint32_t tsb = (uint32_t)ts_b;  // 16 * tsb < 2^31 (checked at the boundary)
+
+  auto issue_tile = [&](int k, auto sc) {
+    const int key0 = 16 * k;
+    const int g0 = seg_of_key(sl, key0);
+    const int nvalid = min(16, sl.n_keys - key0);
+    int d[IPW], row[IPW];
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) d[u] = src_t[u] < nvalid ? src_t[u] : 0;
+    seg_field(sl, p.topk, key0, g0, d, sl.adj, row);
+    const char* base = p.k + uniform64(qoff_b);
+    char* st = stage_buf(sc) + wave * SUB;
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+      const uint64_t off = (uint64_t)(uint32_t)(row[u] + key0 + d[u]) * tsb;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + (off + src_c[u])),
+                                       (__attribute__((address_space(3))) void*)(st + 1024 * u),
+                                       16, 0, 2 /* nt */);
+    }
+  };
+
+  // MFMA operands of the wave's head in a stage (as in attn_shared_kernel)
+  int k_lds[G::KLD], v_lds[VPL];
+#pragma unroll
+  for (int i = 0; i < G::KLD; ++i) k_lds[i] = wave * SUB + 16 * G::chunk_pos(c16, 4 * i + g4);
+  {
+    const int t = 4 * g4 + (c16 >> 2), a = c16 & 3;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int cv = G::CPK / 2 + 2 * j + (a >> 1);
+      v_lds[j] = wave * SUB + 16 * G::chunk_pos(t, cv) + 8 * (a & 1);
+    }
+  }
+
+  f32x4 acc[VPL];
+  float m_run = kNegInf, l_run = 0.f;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (0 < n_tiles) issue_tile(0, std::integral_constant<int, 0>{});
+  if (1 < n_tiles) issue_tile(1, std::integral_constant<int, 1>{});
+  // settle the query fragments behind the first loads, outside the tile loop
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) asm volatile("" ::"v"(qf[i]));
+
+  auto step = [&](auto sc, int k) -> bool {
+    if (k >= n_tiles) return false;
+    wait_tiles_ahead<IPW, 1>(min(1, n_tiles - 1 - k));
+    // every wave's part of tile k has landed (bare s_barrier: a workgroup
+    // fence would also wait for the tile still in flight)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const char* st = stage_buf(sc);
+    Frags<D, QT> f;
+#pragma unroll
+    for (int kc = 0; kc < G::NKC; ++kc) f.kf[kc] = *reinterpret_cast<const u32x4*>(st + k_lds[kc]);
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+      f.vA[j] = bitcast<u32x2>(__builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(st + v_lds[j])));
+    const int key0 = 16 * k;
+    const int nvalid = min(16, sl.n_keys - key0);
+    // bias of the segment of each of the lane's keys 4*g4 + i (the S^T layout)
+    f32x4 kbias;
+    {
+      int d[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[i] = 4 * g4 + i;
+      seg_field(sl, p.topk, key0, seg_of_key(sl, key0), d, __float_as_int(sl.bias), b);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kbias[i] = __int_as_float(b[i]);
+    }
+    // once every wave's reads of the stage have returned, it takes tile k+2;
+    // issued behind the S^T MFMAs, which run while the loads go out
+    auto refill = [&]() {
+      __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (k + 2 < n_tiles) issue_tile(k + 2, sc);
+    };
+    attend_tile<D, QT, false, true, true>(f, qf, acc, m_run, l_run, p.qk_scale_log2, 0.f, nvalid,
+                                          g4, key0, RowMask{false, 0, 0}, refill, NoHook{}, kbias);
+    return true;
+  };
+  for (int k = 0;; k += 2) {
+    if (!step(std::integral_constant<int, 0>{}, k)) break;
+    if (!step(std::integral_constant<int, 1>{}, k + 1)) break;
+  }
+
+  l_run = sum_across_groups(l_run);
+  if (c16 < p.R)
+    store_tile<D, true>(acc, m_run, l_run, p.v_scale, p.out, p.out_kind, p.lse,
+                        (int64_t)n * p.Hq + kvh * p.G + c16, false, g4);
+}
+
 // ---- instantiation table ------------------------------------------------------------
 namespace {
 
@@ -1258,6 +1450,30 @@ bool attention_supported(const LaunchShape& s) { return pick(s) != nullptr; }
 int shared_tile_loads(int D, int kv_kind) {
   const int kb = kv_kind == K_FP8 ? 1 : 2;
   return 16 * 2 * D * kb / 1024;
+}
+
+namespace {
+KernelFn pick_dash(int D, int kv_kind) {
+  if (D == 128 && kv_kind == K_BF16) return dash_shared_kernel<128, K_BF16, kDashHeads>;
+  if (D == 128 && kv_kind == K_FP16) return dash_shared_kernel<128, K_FP16, kDashHeads>;
+  if (D == 64 && kv_kind == K_BF16) return dash_shared_kernel<64, K_BF16, kDashHeads>;
+  if (D == 64 && kv_kind == K_FP16) return dash_shared_kernel<64, K_FP16, kDashHeads>;
+  return nullptr;
+}
+}  // namespace
+
+bool dash_shared_supported(int D, int kv_kind, int G, int Hkv) {
+  return pick_dash(D, kv_kind) != nullptr && G >= 1 && G <= 16 && Hkv % kDashHeads == 0;
+}
+
+hipError_t launch_dash_shared(const AttnParams& p, int D, int kv_kind, hipStream_t stream) {
+  KernelFn fn = pick_dash(D, kv_kind);
+  if (!fn || p.G > 16 || p.R != p.G || p.Hkv % kDashHeads) return hipErrorInvalidValue;
+  const int64_t grid = (int64_t)p.items * (p.Hkv / kDashHeads);
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * kDashHeads), 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnParams& p, const LaunchShape& s, int64_t grid,

@@ -136,6 +136,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // this wave are outstanding (gfx9 encoding: vmcnt[3:0] in bits 3:0 and
 // vmcnt[5:4] in bits 15:14; expcnt = 7 and lgkmcnt = 15 mean "do not wait").
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 0x3) << 14); }
+// s_waitcnt immediate that waits for every LDS / scalar-memory operation of this
+// wave (lgkmcnt = 0) and for nothing else.
+constexpr int kLgkmcnt0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
 
 // Store `n` consecutive floats (n = 4 or 8) converted to the output kind.
 template <int N>

@@ -67,6 +67,13 @@ hipError_t launch_attention(const AttnParams& p, const LaunchShape& s, int64_t g
 
 bool attention_supported(const LaunchShape& s);
 
+// Fused DASH attention with the token rows of kDashHeads kv heads per workgroup
+// staged through LDS (dash_shared_kernel): 16-bit K/V, D = 64 or 128, Hq/Hkv <= 16,
+// Hkv a multiple of kDashHeads.  One workgroup per (query, head group).
+constexpr int kDashHeads = 2;
+bool dash_shared_supported(int D, int kv_kind, int G, int Hkv);
+hipError_t launch_dash_shared(const AttnParams& p, int D, int kv_kind, hipStream_t stream);
+
 hipError_t launch_split_combine(const float* part_o, const float* part_lse, int32_t S,
                                 int32_t rows, int32_t Hq, int32_t D, void* out, int32_t out_kind,
                                 float* lse, hipStream_t stream);
