@@ -525,7 +525,7 @@ __device__ __forceinline__ SegLanes seg_lanes(const AttnParams& p, int n, int la
     const int o = __shfl_up(cum, off, 64);
     if (lane >= off) cum += o;
   }
-  s.n_keys = __shfl(cum, 63, 64);
+  s.n_keys = __builtin_amdgcn_readlane(cum, 63);  // a scalar: tile loops stay uniform
   if (lane < Gs) {
     s.cum_end = cum;
     s.cum_start = cum - u;
@@ -1220,7 +1220,6 @@ void attn_shared_kernel(const AttnParams p) {
 // ================================================================================
 template <int D, int KV, int HP>
 __global__ __launch_bounds__(HP * 64) void dash_shared_kernel(const AttnParams p) {
-  constexpr int NW = HP;
   using G = Geo<D, KV>;
   constexpr int KB = G::KB;
   constexpr int VPL = G::VPL;
@@ -1313,7 +1312,10 @@ __global__ __launch_bounds__(HP * 64) void dash_shared_kernel(const AttnParams p
 
   if (0 < n_tiles) issue_tile(0, std::integral_constant<int, 0>{});
   if (1 < n_tiles) issue_tile(1, std::integral_constant<int, 1>{});
-  // settle the query fragments behind the first loads, outside the tile loop
+  // Settle the query fragments here, outside the tile loop.  This waits for
+  // the two tiles just issued as well; with them still pending at the loop
+  // entry, the compiler's tracking of direct-to-LDS writes loses the stages
+  // apart and drains every load in flight before each read of stage 0.
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) asm volatile("" ::"v"(qf[i]));
 
