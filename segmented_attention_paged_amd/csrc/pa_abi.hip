@@ -15,9 +15,11 @@
 #include "pa_kernels.h"
 #include "pa_plan.h"
 
-// Waves per workgroup of the segment kernels at one 16-row tile per wave: the
-// fused kernel splits a (query, kv head)'s tiles over 4 waves; the two-stage
-// kernel's items (one segment) are a few tiles long and take one wave.
+// Waves per workgroup of attn_kernel's segment modes at one 16-row tile per
+// wave: the fused mode (odd Hkv, or more than 16 query heads per kv head; the
+// rest go to dash_shared_kernel) splits a (query, kv head)'s tiles over 4
+// waves; the two-stage kernel's items (one segment) are a few tiles long and
+// take one wave.
 constexpr int kSegFusedWaves = 4;
 constexpr int kSegWaves = 1;
 

@@ -23,11 +23,14 @@
 // forward: bmm1_scale / bmm2_scale).  Both kernels also come in a causal form:
 // bottom-right causal rows with an exact per-token window.
 //
-// Two kernels:
+// Three kernels:
 //   attn_kernel         waves of a workgroup split the KEYS (round-robin
 //                       tiles, K/V loaded straight into registers one tile
 //                       ahead) and merge their softmax states through LDS.
 //                       Used for <= 16 rows (decode) and the segment modes.
+//   dash_shared_kernel  fused segments: one workgroup per (query, pair of kv
+//                       heads), one wave per head, the pair's token rows
+//                       staged through a two-stage LDS ring.
 //   attn_shared_kernel  waves split the ROWS (one 16-row tile each) and all
 //                       consume the same K/V tiles, which stream through an
 //                       NBUF-stage LDS ring filled by direct-to-LDS loads
