@@ -519,13 +519,19 @@ int segment_attn_run(const void* q, int32_t q_dtype, const void* k, const void* 
   float* part_o = static_cast<float*>(workspace);
   float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * D * 4));
   const int NW = RT == 1 ? kSegWaves : 4 / RT;
-  p.items = N * Gs;
   p.out = part_o;
   p.out_kind = PA_F32;
   p.lse = part_lse;
   p.partial = 1;
-  const LaunchShape ls{D, kv_dtype, q_dtype, RT, NW, MODE_SEGMENT, 0, 0};
-  hipError_t e = launch_attention(p, ls, (int64_t)N * Gs * Hkv * RG, stream);
+  hipError_t e;
+  if (dash_shared_supported(D, kv_dtype, G, Hkv)) {
+    p.items = N;  // one workgroup per (query, kv-head group) walks all its segments
+    e = launch_dash_shared(p, D, kv_dtype, stream);
+  } else {
+    p.items = N * Gs;
+    const LaunchShape ls{D, kv_dtype, q_dtype, RT, NW, MODE_SEGMENT, 0, 0};
+    e = launch_attention(p, ls, (int64_t)N * Gs * Hkv * RG, stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "segment attention launch");
   e = launch_segment_combine(part_o, PA_F32, part_lse, used, bias, N, Gs, Hq, D, out, out_dtype,
                              lse, stream);

@@ -1204,24 +1204,28 @@ void attn_shared_kernel(const AttnParams p) {
 }
 
 // ================================================================================
-// dash_shared_kernel: fused DASH attention (dash_attention page,
-// flash_dash_attention: one query against the valid rows of its gathered
-// segments, each segment's logits shifted by its bias) with the K and V rows of
-// HP kv heads staged through a two-stage LDS ring.
+// dash_shared_kernel: DASH attention (dash_attention page, flash_dash_attention:
+// one query against the valid rows of its gathered segments) with the K and V
+// rows of HP kv heads staged through a two-stage LDS ring.
 //   work item:  (query, group of HP consecutive kv heads); the group's part of
 //               a token row (HP*D contiguous elements of K, the same of V) is
 //               fetched by direct-to-LDS loads of 16-byte chunks.
 //   waves:      HP, wave w serving kv head w of the group (its G query heads
 //               are the rows of one 16-row tile).
-//   keys:       the query's live keys numbered across its segments, 16 per
-//               tile (as the fused mode of attn_kernel); slots past the last
-//               live key fetch the tile's first key and are masked.
+//   fused (PARTS = false): the query's live keys are numbered across its
+//               segments, 16 per tile (as the fused mode of attn_kernel), each
+//               segment's bias is added to its logits and one online softmax
+//               runs over all of them.
+//   partials (PARTS = true): each segment is cut into its own tiles and gets
+//               its own softmax; when its last tile is done the wave writes the
+//               segment's normalised output and LSE (fp32) for the combine.
+//   Slots past a tile's last live key fetch its first key and are masked.
 // Each staged head uses attn_shared_kernel's tile layout (Geo::chunk_pos).
 // Tile k sits in stage k % 2.  A wave reads all of its K and V operands as
 // soon as the tile has landed; once every wave has, the stage takes tile k+2,
 // so two tiles are in flight while a wave computes or waits.
 // ================================================================================
-template <int D, int KV, int HP>
+template <int D, int KV, int HP, bool PARTS>
 __global__ __launch_bounds__(HP * 64) void dash_shared_kernel(const AttnParams p) {
   using G = Geo<D, KV>;
   constexpr int KB = G::KB;
@@ -1249,7 +1253,23 @@ __global__ __launch_bounds__(HP * 64) void dash_shared_kernel(const AttnParams p
   const int kvh = grp * HP + wave;
 
   const SegLanes sl = seg_lanes(p, n, lane);
-  const int n_tiles = (sl.n_keys + 15) >> 4;
+  int n_tiles = (sl.n_keys + 15) >> 4;
+  // partials: lane g also holds segment g's first tile and its tile count
+  int seg_t0 = 0x7fffffff, seg_t1 = 0x7fffffff;  // tiles [seg_t0, seg_t1)
+  if constexpr (PARTS) {
+    const int nt = lane <= p.topk ? (sl.cum_end - sl.cum_start + 15) >> 4 : 0;
+    int cum = nt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(cum, off, 64);
+      if (lane >= off) cum += o;
+    }
+    n_tiles = __builtin_amdgcn_readlane(cum, 63);
+    if (lane <= p.topk) {
+      seg_t1 = cum;
+      seg_t0 = cum - nt;
+    }
+  }
   const int64_t ts_b = p.token_stride * KB;
   // the group's part of the query's first row, in K (V adds the V - K distance)
   const int64_t qoff_b = (int64_t)n * (p.topk * p.bs + p.local) * ts_b +
@@ -1276,14 +1296,33 @@ __global__ __launch_bounds__(HP * 64) void dash_shared_kernel(const AttnParams p
   }
   const uint32_t tsb = (uint32_t)ts_b;  // 16 * tsb < 2^31 (checked at the boundary)
 
+  // partials: segment of tile k, the tile's first row within the query and
+  // its live keys
+  auto part_tile = [&](int k, int& g, int& row0, int& nvalid) {
+    g = __builtin_amdgcn_readfirstlane(__builtin_popcountll(__ballot(seg_t1 <= k)));
+    const int j = k - __builtin_amdgcn_readlane(seg_t0, g);
+    row0 = __builtin_amdgcn_readlane(sl.adj + sl.cum_start, g) + 16 * j;
+    nvalid = min(16, __builtin_amdgcn_readlane(sl.cum_end - sl.cum_start, g) - 16 * j);
+  };
   auto issue_tile = [&](int k, auto sc) {
-    const int key0 = 16 * k;
-    const int g0 = seg_of_key(sl, key0);
-    const int nvalid = min(16, sl.n_keys - key0);
-    int d[IPW], row[IPW];
+    int key0, nvalid, d[IPW], row[IPW];
+    if constexpr (PARTS) {
+      int g, row0;
+      part_tile(k, g, row0, nvalid);
+      key0 = 0;
 #pragma unroll
-    for (int u = 0; u < IPW; ++u) d[u] = src_t[u] < nvalid ? src_t[u] : 0;
-    seg_field(sl, p.topk, key0, g0, d, sl.adj, row);
+      for (int u = 0; u < IPW; ++u) {
+        d[u] = src_t[u] < nvalid ? src_t[u] : 0;
+        row[u] = row0;
+      }
+    } else {
+      key0 = 16 * k;
+      const int g0 = seg_of_key(sl, key0);
+      nvalid = min(16, sl.n_keys - key0);
+#pragma unroll
+      for (int u = 0; u < IPW; ++u) d[u] = src_t[u] < nvalid ? src_t[u] : 0;
+      seg_field(sl, p.topk, key0, g0, d, sl.adj, row);
+    }
     const char* base = p.k + uniform64(qoff_b);
     char* st = stage_buf(sc) + wave * SUB;
 #pragma unroll
@@ -1338,11 +1377,19 @@ __global__ __launch_bounds__(HP * 64) void dash_shared_kernel(const AttnParams p
     for (int j = 0; j < VPL; ++j)
       f.vA[j] = bitcast<u32x2>(__builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) i16x4*)(st + v_lds[j])));
-    const int key0 = 16 * k;
-    const int nvalid = min(16, sl.n_keys - key0);
-    // bias of the segment of each of the lane's keys 4*g4 + i (the S^T layout)
-    f32x4 kbias;
-    {
+    int key0 = 16 * k, nvalid, g = 0, row0 = 0;
+    f32x4 kbias = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (PARTS) {
+      part_tile(k, g, row0, nvalid);
+      if (k == __builtin_amdgcn_readlane(seg_t0, g)) {  // a segment starts: fresh softmax
+        m_run = kNegInf;
+        l_run = 0.f;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    } else {
+      nvalid = min(16, sl.n_keys - key0);
+      // bias of the segment of each of the lane's keys 4*g4 + i (the S^T layout)
       int d[4], b[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) d[i] = 4 * g4 + i;
@@ -1359,8 +1406,17 @@ __global__ __launch_bounds__(HP * 64) void dash_shared_kernel(const AttnParams p
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       if (k + 2 < n_tiles) issue_tile(k + 2, sc);
     };
-    attend_tile<D, QT, false, true, true>(f, qf, acc, m_run, l_run, p.qk_scale_log2, 0.f, nvalid,
-                                          g4, key0, RowMask{false, 0, 0}, refill, NoHook{}, kbias);
+    attend_tile<D, QT, false, !PARTS, !PARTS>(f, qf, acc, m_run, l_run, p.qk_scale_log2, 0.f,
+                                              nvalid, g4, key0, RowMask{false, 0, 0}, refill,
+                                              NoHook{}, kbias);
+    if constexpr (PARTS) {
+      if (k + 1 == __builtin_amdgcn_readlane(seg_t1, g)) {  // the segment's last tile
+        const float l_tot = sum_across_groups(l_run);
+        if (c16 < p.R)
+          store_tile<D, true>(acc, m_run, l_tot, p.v_scale, p.out, p.out_kind, p.lse,
+                              ((int64_t)n * (p.topk + 1) + g) * p.Hq + kvh * p.G + c16, true, g4);
+      }
+    }
     return true;
   };
   for (int k = 0;; k += 2) {
@@ -1368,10 +1424,12 @@ __global__ __launch_bounds__(HP * 64) void dash_shared_kernel(const AttnParams p
     if (!step(std::integral_constant<int, 1>{}, k + 1)) break;
   }
 
-  l_run = sum_across_groups(l_run);
-  if (c16 < p.R)
-    store_tile<D, true>(acc, m_run, l_run, p.v_scale, p.out, p.out_kind, p.lse,
-                        (int64_t)n * p.Hq + kvh * p.G + c16, false, g4);
+  if constexpr (!PARTS) {
+    l_run = sum_across_groups(l_run);
+    if (c16 < p.R)
+      store_tile<D, true>(acc, m_run, l_run, p.v_scale, p.out, p.out_kind, p.lse,
+                          (int64_t)n * p.Hq + kvh * p.G + c16, false, g4);
+  }
 }
 
 // ---- instantiation table ------------------------------------------------------------
@@ -1458,21 +1516,25 @@ int shared_tile_loads(int D, int kv_kind) {
 }
 
 namespace {
-KernelFn pick_dash(int D, int kv_kind) {
-  if (D == 128 && kv_kind == K_BF16) return dash_shared_kernel<128, K_BF16, kDashHeads>;
-  if (D == 128 && kv_kind == K_FP16) return dash_shared_kernel<128, K_FP16, kDashHeads>;
-  if (D == 64 && kv_kind == K_BF16) return dash_shared_kernel<64, K_BF16, kDashHeads>;
-  if (D == 64 && kv_kind == K_FP16) return dash_shared_kernel<64, K_FP16, kDashHeads>;
+template <bool PARTS>
+KernelFn pick_dash_mode(int D, int kv_kind) {
+  if (D == 128 && kv_kind == K_BF16) return dash_shared_kernel<128, K_BF16, kDashHeads, PARTS>;
+  if (D == 128 && kv_kind == K_FP16) return dash_shared_kernel<128, K_FP16, kDashHeads, PARTS>;
+  if (D == 64 && kv_kind == K_BF16) return dash_shared_kernel<64, K_BF16, kDashHeads, PARTS>;
+  if (D == 64 && kv_kind == K_FP16) return dash_shared_kernel<64, K_FP16, kDashHeads, PARTS>;
   return nullptr;
+}
+KernelFn pick_dash(int D, int kv_kind, bool parts) {
+  return parts ? pick_dash_mode<true>(D, kv_kind) : pick_dash_mode<false>(D, kv_kind);
 }
 }  // namespace
 
 bool dash_shared_supported(int D, int kv_kind, int G, int Hkv) {
-  return pick_dash(D, kv_kind) != nullptr && G >= 1 && G <= 16 && Hkv % kDashHeads == 0;
+  return pick_dash(D, kv_kind, false) != nullptr && G >= 1 && G <= 16 && Hkv % kDashHeads == 0;
 }
 
 hipError_t launch_dash_shared(const AttnParams& p, int D, int kv_kind, hipStream_t stream) {
-  KernelFn fn = pick_dash(D, kv_kind);
+  KernelFn fn = pick_dash(D, kv_kind, p.partial != 0);
   if (!fn || p.G > 16 || p.R != p.G || p.Hkv % kDashHeads) return hipErrorInvalidValue;
   const int64_t grid = (int64_t)p.items * (p.Hkv / kDashHeads);
   if (grid <= 0) return hipSuccess;
