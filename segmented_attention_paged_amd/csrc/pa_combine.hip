@@ -10,10 +10,12 @@
 // One thread per V consecutive head-dim values of one (row, head).  Each
 // thread reads the partial logits itself (the D/V threads of a row share them
 // through the cache), so there is no cross-lane step, and it fetches the
-// partial rows in batches of kBatch independent loads, issued together with
-// the logits.  Batches are merged with a running maximum.  A dead partial's
-// row (possibly never written) only ever meets a select, so it cannot leak
-// into the result.
+// partial rows in batches of independent loads (8 Split-KV partials, 16 DASH
+// segments), issued together with the logits and everything the logits need
+// (segment lengths and biases are loaded unconditionally and selected
+// afterwards, so a batch costs one round trip).  Batches are merged with a
+// running maximum.  A dead partial's row and LSE (possibly never written)
+// only ever meet a select, so they cannot leak into the result.
 
 #include "pa_device.h"
 #include "pa_kernels.h"
@@ -24,7 +26,21 @@ namespace pa {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kBatch = 8;
+constexpr int kSplitBatch = 8;
+constexpr int kSegmentBatch = 16;
+
+// What the logit of one partial is formed from; settle() pins the loaded
+// fields (an empty asm that reads them), so their loads are issued, and
+// waited for, where the batch settles rather than inside a select's branch.
+struct LseRaw {
+  float lse;
+  __device__ void settle() { asm volatile("" ::"v"(lse)); }
+};
+struct SegRaw {
+  int used;
+  float lse, bias;
+  __device__ void settle() { asm volatile("" ::"v"(used), "v"(lse), "v"(bias)); }
+};
 
 template <int V, int PK>
 __device__ __forceinline__ void load_vec(const void* base, int64_t i, float (&x)[V]) {
@@ -65,24 +81,34 @@ __device__ __forceinline__ void store_vec(void* base, int64_t i, int kind, const
   }
 }
 
-// Merge G partials of one (row, head) for this thread's V values.  logit(g)
-// is the natural-log logit of partial g (-inf: dead); load(g, x) fetches its
-// values.  Returns the weighted mean in o and the merged LSE.
-template <int V, typename LogitFn, typename LoadFn>
-__device__ __forceinline__ float merge_partials(int G, LogitFn logit, LoadFn load, float (&o)[V]) {
+// Merge G partials of one (row, head) for this thread's V values.
+// fetch(g) loads what the logit of partial g needs (a small struct with a
+// settle() that pins its loaded fields), logit(raw, g) turns it into the
+// natural-log logit (-inf: dead), load(g, x) fetches the partial's values.
+// A batch issues every load first and settles them all before any logit is
+// formed, so no load ends up behind a test of another (the compiler would
+// otherwise move a load used on one side of a select into a branch, after a
+// wait for the select's condition).  Returns the weighted mean in o and the
+// merged LSE.
+template <int V, int kBatch, typename FetchFn, typename LogitFn, typename LoadFn>
+__device__ __forceinline__ float merge_partials(int G, FetchFn fetch, LogitFn logit, LoadFn load,
+                                                float (&o)[V]) {
   float m = kNegInf, l = 0.f;
 #pragma unroll
   for (int i = 0; i < V; ++i) o[i] = 0.f;
   for (int g0 = 0; g0 < G; g0 += kBatch) {
+    decltype(fetch(0)) raw[kBatch];
     float lg[kBatch], x[kBatch][V];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const bool in = g0 + u < G;
-      const int g = in ? g0 + u : g0;  // past the end: a valid index, weight forced to 0
-      const float lv = logit(g);
-      lg[u] = in ? lv : kNegInf;
+      const int g = g0 + u < G ? g0 + u : g0;  // past the end: a valid index, weight forced to 0
+      raw[u] = fetch(g);
       load(g, x[u]);
     }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) raw[u].settle();
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) lg[u] = g0 + u < G ? logit(raw[u], g0 + u) : kNegInf;
     float mb = m;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) mb = fmaxf(mb, lg[u]);
@@ -120,12 +146,13 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const float* __restr
   const int64_t rh = t / tpr;  // row * Hq + head
   if (rh >= total) return;
   const int d0 = (int)(t - rh * tpr) * V;
-  auto logit = [&](int s) -> float { return part_lse[(int64_t)s * total + rh]; };
+  auto fetch = [&](int s) { return LseRaw{part_lse[(int64_t)s * total + rh]}; };
+  auto logit = [](const LseRaw& r, int) { return r.lse; };
   auto load = [&](int s, float (&x)[V]) {
     load_vec<V, K_F32>(part_o, ((int64_t)s * total + rh) * D + d0, x);
   };
   float o[V];
-  const float L = merge_partials<V>(S, logit, load, o);
+  const float L = merge_partials<V, kSplitBatch>(S, fetch, logit, load, o);
   store_vec<V>(out, rh * D + d0, out_kind, o);
   if (lse && d0 == 0) lse[rh] = L;
 }
@@ -142,16 +169,21 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(
   const int d0 = (int)(t - nh * tpr) * V;
   const int64_t n = nh / Hq;
   const int h = (int)(nh - n * Hq);
-  auto logit = [&](int g) -> float {
-    if (used[n * G + g] <= 0) return kNegInf;
-    const float prior = g < G - 1 ? bias[n * (G - 1) + g] : 0.f;
-    return part_lse[(n * G + g) * Hq + h] + prior;
+  // Without remote segments there is no bias row (the pointer may be NULL):
+  // the bias load then rereads the LSE row and is dropped, as it is for the
+  // local segment (g = G - 1), which rereads the last remote bias.
+  const float* brow = G > 1 ? bias + n * (G - 1) : part_lse;
+  auto fetch = [&](int g) {
+    return SegRaw{used[n * G + g], part_lse[(n * G + g) * Hq + h], brow[g < G - 1 ? g : (G > 1 ? G - 2 : 0)]};
+  };
+  auto logit = [&](const SegRaw& r, int g) {
+    return r.used <= 0 ? kNegInf : r.lse + (g < G - 1 ? r.bias : 0.f);
   };
   auto load = [&](int g, float (&x)[V]) {
     load_vec<V, PK>(part_o, ((n * G + g) * Hq + h) * D + d0, x);
   };
   float o[V];
-  const float L = merge_partials<V>(G, logit, load, o);
+  const float L = merge_partials<V, kSegmentBatch>(G, fetch, logit, load, o);
   store_vec<V>(out, nh * D + d0, out_kind, o);
   if (lse && d0 == 0) lse[nh] = L;
 }
