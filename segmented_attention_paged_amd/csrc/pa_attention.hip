@@ -2,9 +2,10 @@
 //
 // Rows of a work item are the G query heads of one kv head times the query
 // block (row r -> token r / G, head kvh*G + r % G), packed into 16-row MFMA
-// tiles.  Keys are consumed in tiles of 16 slots of one page (paged modes), of
-// one segment (segment partials), or of a query's live keys numbered across its
-// segments (fused segments: a tile may span segments).
+// tiles.  Keys are consumed in tiles of 16 slots of one page (paged modes; the
+// dense fp8-query block pairs two such tiles), of one segment (segment
+// partials), or of a query's live keys numbered across its segments (fused
+// segments: a tile may span segments).
 //
 // Per 16-key tile and 16-row tile:
 //   S^T = K Q^T      D/32 x v_mfma_f32_16x16x32_{bf16,f16}, or _fp8_fp8 on the
@@ -376,6 +377,64 @@ __device__ __forceinline__ void attend_tile(const Frags<D, QT>& f,
   }
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) acc[j] = mfma_16x16x16<PV>(f.vA[j], pB, acc[j]);
+}
+
+// Two 16-key tiles (keys 0..15 in f0, 16..31 in f1) against one 16-row tile,
+// with one softmax update and P.V on the 32-deep MFMA: its contraction index
+// 8*(l/16) + j pairs keys 4*(l/16) + j of the first tile (j < 4) with keys
+// 16 + 4*(l/16) + j - 4 of the second, so A and B are the two 16-key operands
+// side by side.  Every row has a live key in the first tile (no causal mask).
+template <int D, int QT, typename Hook, typename VHook, typename VOp>
+__device__ __forceinline__ void attend_tile32(const Frags<D, QT>& f0, const Frags<D, QT>& f1,
+                                              const typename QTypes<QT>::QOp (&qf)[D / 32],
+                                              f32x4 (&acc)[D / 16], float& m_run, float& l_run,
+                                              float scale_log2, int nvalid0, int nvalid1, int g4,
+                                              const Hook& mid, const VHook& vload, const VOp& vop) {
+  f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kc = 0; kc < D / 32; ++kc) sa = qk_mfma<QT>(f0.kf[kc], qf[kc], sa);
+#pragma unroll
+  for (int kc = 0; kc < D / 32; ++kc) sb = qk_mfma<QT>(f1.kf[kc], qf[kc], sb);
+  float s[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s[i] = sa[i] * scale_log2;
+    s[4 + i] = sb[i] * scale_log2;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  mid();
+  __builtin_amdgcn_sched_barrier(0);
+  if (nvalid0 < 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * g4 + i >= nvalid0) s[i] = kNegInf;
+  }
+  if (nvalid1 < 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * g4 + i >= nvalid1) s[4 + i] = kNegInf;
+  }
+  float tmax = vmax(vmax(vmax(s[0], s[1]), vmax(s[2], s[3])), vmax(vmax(s[4], s[5]), vmax(s[6], s[7])));
+  tmax = max_across_groups(tmax);
+  if (__ballot(tmax > m_run + kRescaleSlack) != 0) {
+    const float m_new = vmax(m_run, tmax);
+    const float alpha = fast_exp2(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) acc[j] *= alpha;
+    m_run = m_new;
+  }
+  float pr[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(s[i] - m_run);
+  l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+  constexpr int PV = QTypes<QT>::PV;
+  const u32x4 pB = u32x4{pack2<PV>(pr[0], pr[1]), pack2<PV>(pr[2], pr[3]), pack2<PV>(pr[4], pr[5]),
+                         pack2<PV>(pr[6], pr[7])};
+  __builtin_amdgcn_sched_barrier(0);
+  vload();
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) acc[j] = mfma_16x16x32<PV>(vop(j), pB, acc[j]);
 }
 
 // Write one lane's part of a finished 16-row tile: row row0 + l%16, values
@@ -901,27 +960,33 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams p) {
 template <int NW, int QT>
 constexpr int kSharedMinWaves = NW >= 4 ? (QT == K_FP8 ? 6 : 5) : 1;
 
-template <int D, int NW, int KV, int QT, int NBUF, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSharedMinWaves<NW, QT>)))
+// KT: keys per staged tile.  The dense fp8-query block stages 32 keys (two
+// 16-key sub-tiles, each from its own page slot range) and runs attend_tile32:
+// one softmax update and half as many P.V MFMAs per key at the full 32-deep
+// rate, for five instead of six waves per SIMD (84 VGPRs).
+template <int D, int NW, int KV, int QT, int NBUF, bool CAUSAL, int KT = 16>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KT == 32 ? 5 : kSharedMinWaves<NW, QT>)))
 void attn_shared_kernel(const AttnParams p) {
   using G = Geo<D, KV>;
   constexpr int KB = G::KB;
   constexpr int VPL = G::VPL;
-  constexpr int IPW = G::IPT / NW;  // direct-to-LDS loads per wave per tile
-  static_assert(G::IPT % NW == 0 && IPW >= 1, "tile loads must split evenly over the waves");
+  static_assert(KT == 16 || (KT == 32 && !CAUSAL), "32-key tiles without the causal mask");
+  constexpr int TB = G::TILE_BYTES * (KT / 16);  // bytes of a staged tile
+  constexpr int IPW = TB / 1024 / NW;  // direct-to-LDS loads per wave per tile
+  static_assert((TB / 1024) % NW == 0 && IPW >= 1, "tile loads must split evenly over the waves");
   static_assert(NBUF >= 2 && NBUF <= 8, "ring depth");
   // One LDS object per ring stage, addressed with compile-time stage numbers
   // (the tile loop is unrolled NBUF times).  The compiler can then tell that
   // reading stage s does not depend on the direct-to-LDS loads still landing
   // in the other stages; with a single array it waits for all of them first.
-  __shared__ __attribute__((aligned(1024))) char ring0[G::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char ring1[G::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char ring2[NBUF > 2 ? G::TILE_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) char ring3[NBUF > 3 ? G::TILE_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) char ring4[NBUF > 4 ? G::TILE_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) char ring5[NBUF > 5 ? G::TILE_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) char ring6[NBUF > 6 ? G::TILE_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) char ring7[NBUF > 7 ? G::TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char ring0[TB];
+  __shared__ __attribute__((aligned(1024))) char ring1[TB];
+  __shared__ __attribute__((aligned(1024))) char ring2[NBUF > 2 ? TB : 16];
+  __shared__ __attribute__((aligned(1024))) char ring3[NBUF > 3 ? TB : 16];
+  __shared__ __attribute__((aligned(1024))) char ring4[NBUF > 4 ? TB : 16];
+  __shared__ __attribute__((aligned(1024))) char ring5[NBUF > 5 ? TB : 16];
+  __shared__ __attribute__((aligned(1024))) char ring6[NBUF > 6 ? TB : 16];
+  __shared__ __attribute__((aligned(1024))) char ring7[NBUF > 7 ? TB : 16];
   auto stage_buf = [&](auto sc) -> char* {
     constexpr int s = decltype(sc)::value;
     if constexpr (s == 0) return ring0;
@@ -950,7 +1015,7 @@ void attn_shared_kernel(const AttnParams p) {
   const int64_t ts_b = p.token_stride * KB;
   const int64_t head_off_b = (int64_t)kvh * p.head_stride * KB;
   const PagedRange pr = paged_range(p, item, split);
-  const int n_tiles = pr.n_tiles;
+  const int n_tiles = KT == 32 ? (pr.n_tiles + 1) >> 1 : pr.n_tiles;  // 16-key sub-tiles paired
   const int row0 = rg * (NW * 16) + wave * 16;
 
   typename QTypes<QT>::QOp qf[D / 32];
@@ -978,15 +1043,17 @@ void attn_shared_kernel(const AttnParams p) {
   // fetched instead when key t is past the end of a partial tile.
   const int64_t vk = p.v - p.k;
   int64_t src_slot0[IPW], src_key_off[IPW];
-  int src_key[IPW];
+  int src_key[IPW], src_half[IPW];
 #pragma unroll
   for (int u = 0; u < IPW; ++u) {
     const int pos = 64 * (wave * IPW + u) + lane;
-    const int t = pos / G::CPK;
+    const int tt = pos / G::CPK;
+    const int t = tt & 15;
     const int c = (pos % G::CPK) ^ G::swz(t, pos % G::CPK);  // chunk_pos is an involution per key
     src_slot0[u] = c < G::CPK / 2 ? 16 * c : vk + 16 * (c - G::CPK / 2);
     src_key_off[u] = t * ts_b;
     src_key[u] = t;
+    src_half[u] = __builtin_amdgcn_readfirstlane(tt >> 4);  // one 16-key half per load
   }
   const int64_t page_b = p.page_stride * KB;
   const int TPP = pr.TPP;
@@ -1013,21 +1080,55 @@ void attn_shared_kernel(const AttnParams p) {
   };
 
   auto issue_tile = [&](int k, const Cursor& c, auto sc) {
-    if (k - k0 >= 64) {  // next batch: waits for its table load (once per 64 tiles)
-      k0 = k;
-      phys_vec = table_batch(k0);
-    }
-    int32_t phys = __builtin_amdgcn_readlane(phys_vec, k - k0);
-    phys = phys < 0 ? 0 : (phys >= p.num_pages ? p.num_pages - 1 : phys);
     char* ring = stage_buf(sc);
-    const char* tile = p.k + ((int64_t)phys * page_b + (int64_t)(16 * c.u) * ts_b + head_off_b);
-    const int nvalid = cursor_valid(c);
+    if constexpr (KT == 16) {
+      if (k - k0 >= 64) {  // next batch: waits for its table load (once per 64 tiles)
+        k0 = k;
+        phys_vec = table_batch(k0);
+      }
+      int32_t phys = __builtin_amdgcn_readlane(phys_vec, k - k0);
+      phys = phys < 0 ? 0 : (phys >= p.num_pages ? p.num_pages - 1 : phys);
+      const char* tile = p.k + ((int64_t)phys * page_b + (int64_t)(16 * c.u) * ts_b + head_off_b);
+      const int nvalid = cursor_valid(c);
 #pragma unroll
-    for (int u = 0; u < IPW; ++u) {
-      const int64_t off = src_slot0[u] + ((nvalid == 16 || src_key[u] < nvalid) ? src_key_off[u] : 0);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(tile + off),
-                                       (__attribute__((address_space(3))) void*)(ring + 1024 * (wave * IPW + u)),
-                                       16, 0, 2 /* nt */);
+      for (int u = 0; u < IPW; ++u) {
+        const int64_t off = src_slot0[u] + ((nvalid == 16 || src_key[u] < nvalid) ? src_key_off[u] : 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(tile + off),
+                                         (__attribute__((address_space(3))) void*)(ring + 1024 * (wave * IPW + u)),
+                                         16, 0, 2 /* nt */);
+      }
+    } else {
+      // sub-tiles 2k and 2k+1 (the batch is refilled at even sub-tiles, so both
+      // are in it)
+      const int ks = 2 * k;
+      if (ks - k0 >= 64) {
+        k0 = ks;
+        phys_vec = table_batch(k0);
+      }
+      Cursor c1 = c;
+      advance(c1);
+      const char* tile[2];
+      int nv[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int32_t phys = __builtin_amdgcn_readlane(phys_vec, ks + h - k0);
+        phys = phys < 0 ? 0 : (phys >= p.num_pages ? p.num_pages - 1 : phys);
+        const Cursor& ch = h == 0 ? c : c1;
+        tile[h] = p.k + ((int64_t)phys * page_b + (int64_t)(16 * ch.u) * ts_b + head_off_b);
+        nv[h] = cursor_valid(ch);
+      }
+      // a second sub-tile past the end re-reads the first one's slot 0: its
+      // page is not the request's (a table pad may point anywhere)
+      if (nv[1] <= 0) tile[1] = tile[0];
+#pragma unroll
+      for (int u = 0; u < IPW; ++u) {
+        const int h = src_half[u];
+        const int nvalid = h == 0 ? nv[0] : nv[1];
+        const int64_t off = src_slot0[u] + ((nvalid == 16 || src_key[u] < nvalid) ? src_key_off[u] : 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>((h == 0 ? tile[0] : tile[1]) + off),
+                                         (__attribute__((address_space(3))) void*)(ring + 1024 * (wave * IPW + u)),
+                                         16, 0, 2 /* nt */);
+      }
     }
   };
 
@@ -1071,8 +1172,8 @@ void attn_shared_kernel(const AttnParams p) {
       v_lds[pp] = 16 * G::chunk_pos(t, cv) + 8 * a;
     }
   }
-  auto read_k = [&](auto sc, Frags<D, QT>& f) {
-    const char* st = stage_buf(sc);
+  auto read_k = [&](auto sc, Frags<D, QT>& f, int hoff = 0) {
+    const char* st = stage_buf(sc) + hoff;
     if constexpr (TR) {
 #pragma unroll
       for (int kc = 0; kc < G::NKC; ++kc) f.kf[kc] = *reinterpret_cast<const u32x4*>(st + k_lds[kc]);
@@ -1083,8 +1184,8 @@ void attn_shared_kernel(const AttnParams p) {
       k_operands<D, KV, QT>(rk, f);
     }
   };
-  auto read_v = [&](auto sc, Frags<D, QT>& f) {
-    const char* st = stage_buf(sc);
+  auto read_v = [&](auto sc, Frags<D, QT>& f, int hoff = 0) {
+    const char* st = stage_buf(sc) + hoff;
     if constexpr (TR) {
 #pragma unroll
       for (int j = 0; j < VPL; ++j)
@@ -1128,6 +1229,7 @@ void attn_shared_kernel(const AttnParams p) {
       if (s < n_tiles) {
         issue_tile(s, ci, sc);
         advance(ci);
+        if constexpr (KT == 32) advance(ci);
       }
     }
   };
@@ -1163,11 +1265,40 @@ void attn_shared_kernel(const AttnParams p) {
       if (k + NBUF - 1 < n_tiles) {
         issue_tile(k + NBUF - 1, ci, std::integral_constant<int, (s + NBUF - 1) % NBUF>{});
         advance(ci);
+        if constexpr (KT == 32) advance(ci);
       }
     };
     const int nvalid = cursor_valid(cc);
     const int key0 = cc.tok0;
     advance(cc);
+    if constexpr (KT == 32) {
+      const int nvalid1 = cursor_valid(cc);
+      advance(cc);
+      Frags<D, QT> f0, f1;
+      read_k(sc, f0);
+      read_k(sc, f1, G::TILE_BYTES);
+      // V^T stays fp8 in registers until each P.V MFMA converts its own part
+      v2i32 rv[2][VPL / 2];
+      auto vload = [&]() {
+        const char* st = stage_buf(sc);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int pp = 0; pp < VPL / 2; ++pp)
+            rv[h][pp] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) v2i32*)(st + h * G::TILE_BYTES + v_lds[pp]));
+      };
+      auto vop = [&](int j) -> u32x4 {
+        constexpr int PV = QTypes<QT>::PV;
+        uint32_t a0, a1, b0, b1;
+        fp8x4_to_16<PV>((uint32_t)rv[0][j >> 1][j & 1], a0, a1);
+        fp8x4_to_16<PV>((uint32_t)rv[1][j >> 1][j & 1], b0, b1);
+        return u32x4{a0, a1, b0, b1};
+      };
+      attend_tile32<D, QT>(f0, f1, qf, acc, m_run, l_run, p.qk_scale_log2, nvalid, nvalid1, g4, refill,
+                           vload, vop);
+      return true;
+    }
     Frags<D, QT> f;
     const bool on = CAUSAL && (key0 + 15 > hi_min || key0 < lo_max);
     // V^T is read only after the softmax, so it is not live across it: 96
@@ -1457,11 +1588,13 @@ KernelFn pick_keys(int RT, int NW) {
 template <int D, int KV, int QT, bool C>
 KernelFn pick_rows(int NW) {
   constexpr int IPT = Geo<D, KV>::IPT;
-  if constexpr (IPT % 8 == 0)
-    if (NW == 8) return attn_shared_kernel<D, 8, KV, QT, kRingStages, C>;
-  if constexpr (IPT % 4 == 0)
-    if (NW == 4) return attn_shared_kernel<D, 4, KV, QT, kRingStages, C>;
-  if (NW == 2) return attn_shared_kernel<D, 2, KV, QT, kRingStages, C>;
+  constexpr int KT = (QT == K_FP8 && !C) ? 32 : 16;
+  constexpr int IPT2 = IPT * KT / 16;
+  if constexpr (IPT2 % 8 == 0)
+    if (NW == 8) return attn_shared_kernel<D, 8, KV, QT, kRingStages, C, KT>;
+  if constexpr (IPT2 % 4 == 0)
+    if (NW == 4) return attn_shared_kernel<D, 4, KV, QT, kRingStages, C, KT>;
+  if (NW == 2) return attn_shared_kernel<D, 2, KV, QT, kRingStages, C, KT>;
   return nullptr;
 }
 
