@@ -1035,17 +1035,27 @@ void attn_shared_kernel(const AttnParams p) {
   };
   int32_t phys_vec = table_batch(0);
   int k0 = 0;
-  // 32-key tiles: lane i holds the byte offset of sub-tile k0 + i's page
-  // (clamped into the pool), worked out once per 64 sub-tiles, so a tile's two
-  // page addresses cost two v_readlane pairs instead of scalar clamps and
-  // 64-bit multiplies (fp8-query block ~1% faster)
-  const int64_t page_b0 = p.page_stride * KB;
-  auto page_offsets = [&](int32_t ph) -> int64_t {
-    ph = ph < 0 ? 0 : (ph >= p.num_pages ? p.num_pages - 1 : ph);
-    return (int64_t)ph * page_b0;
-  };
+  // 32-key tiles: lane i holds the byte offset (pool page, clamped, and slot)
+  // and the live slots of sub-tile k0 + i, worked out once per 64 sub-tiles,
+  // so issuing a tile takes six v_readlane instead of a cursor walk, scalar
+  // clamps and 64-bit multiplies (fp8-query block 3-4% faster)
   int64_t poff_vec = 0;
-  if constexpr (KT == 32) poff_vec = page_offsets(phys_vec);
+  int nv_vec = 0;
+  auto sub_batch = [&](int first, int32_t ph) {
+    ph = ph < 0 ? 0 : (ph >= p.num_pages ? p.num_pages - 1 : ph);
+    const int j = first + lane;
+    int tpp = pr.TPP;
+    asm volatile("" : "+s"(tpp));
+    const int pg = tpp == 1 ? j : j / tpp;
+    const int u = j - pg * tpp;
+    const int tok0 = (pr.sr.first_page + pg) * p.P + 16 * u;
+    int nv = p.P - 16 * u;
+    nv = nv > 16 ? 16 : nv;
+    nv = pr.tok_end - tok0 < nv ? pr.tok_end - tok0 : nv;
+    poff_vec = (int64_t)ph * (p.page_stride * KB) + (int64_t)(16 * u) * ts_b;
+    nv_vec = nv;
+  };
+  if constexpr (KT == 32) sub_batch(0, phys_vec);
 
   // Lane-constant part of the source address of each chunk this wave copies:
   // instruction j = wave*IPW + u writes LDS position 64*j + lane, which holds
@@ -1114,19 +1124,16 @@ void attn_shared_kernel(const AttnParams p) {
       const int ks = 2 * k;
       if (ks - k0 >= 64) {
         k0 = ks;
-        poff_vec = page_offsets(table_batch(k0));
+        sub_batch(k0, table_batch(k0));
       }
-      Cursor c1 = c;
-      advance(c1);
       const char* tile[2];
       int nv[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)poff_vec, ks + h - k0);
         const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)poff_vec >> 32), ks + h - k0);
-        const Cursor& ch = h == 0 ? c : c1;
-        tile[h] = p.k + ((int64_t)(((uint64_t)hi << 32) | lo) + (int64_t)(16 * ch.u) * ts_b + head_off_b);
-        nv[h] = cursor_valid(ch);
+        tile[h] = p.k + ((int64_t)(((uint64_t)hi << 32) | lo) + head_off_b);
+        nv[h] = __builtin_amdgcn_readlane(nv_vec, ks + h - k0);
       }
       // a second sub-tile past the end re-reads the first one's slot 0: its
       // page is not the request's (a table pad may point anywhere)
@@ -1239,8 +1246,7 @@ void attn_shared_kernel(const AttnParams p) {
     if constexpr (s < NBUF - 1) {
       if (s < n_tiles) {
         issue_tile(s, ci, sc);
-        advance(ci);
-        if constexpr (KT == 32) advance(ci);
+        if constexpr (KT == 16) advance(ci);
       }
     }
   };
@@ -1275,8 +1281,7 @@ void attn_shared_kernel(const AttnParams p) {
     auto refill = [&]() {
       if (k + NBUF - 1 < n_tiles) {
         issue_tile(k + NBUF - 1, ci, std::integral_constant<int, (s + NBUF - 1) % NBUF>{});
-        advance(ci);
-        if constexpr (KT == 32) advance(ci);
+        if constexpr (KT == 16) advance(ci);
       }
     };
     const int nvalid = cursor_valid(cc);
