@@ -28,6 +28,11 @@ CASES = {
     "sq16_g4": dict(B=3, sq=16, Hq=32, Hkv=8, D=128, P=16, seq_lens=[16, 257, 640]),
     "sq16_d64_page64": dict(B=2, sq=16, Hq=8, Hkv=2, D=64, P=64, seq_lens=[20, 400]),
     "sq3_rt2": dict(B=3, sq=3, Hq=8, Hkv=1, D=128, P=16, seq_lens=[3, 50, 333]),
+    # query blocks staged 32 keys at a time (two 16-slot sub-tiles): pages of 8
+    # slots (one short sub-tile per page) and of 48 (three sub-tiles per page,
+    # so a tile's two halves may sit in different pages), odd sub-tile counts
+    "sq16_page8": dict(B=2, sq=16, Hq=8, Hkv=2, D=128, P=8, seq_lens=[17, 333]),
+    "sq16_page48": dict(B=3, sq=16, Hq=8, Hkv=2, D=128, P=48, seq_lens=[16, 100, 481]),
 }
 
 
